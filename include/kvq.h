@@ -1,0 +1,223 @@
+/*
+ * kvq.h — C ABI of the low-bit KV-cache library for MI355X (gfx950).
+ *
+ * What it computes
+ *   Asymmetric affine integer codes for a transformer's key/value cache and
+ *   single-token decode attention that reads the packed codes and dequantizes
+ *   them inside the attention kernel.
+ *
+ *   - Affine quantizer: q = round(x / scale) + zero_point, x_hat = scale * (q -
+ *     zero_point), scale = (x_max - x_min) / (q_max - q_min), zero_point =
+ *     q_min - round(x_min / scale); int8 range [-128, 127], int4 [-8, 7].
+ *     ("KV Cache Quantization — 8-bit and 4-bit", section "Integer quantization
+ *     in one screen".)  int2 uses [-2, 1]: the four levels that "Sub-8-Bit KV
+ *     Cache Quantization Is Not a Free Lever for an RDNA4 Agent Swarm" names in
+ *     "Why 8 bits hides the problem and 4 bits exposes it".
+ *   - Axis split: values per token; keys per token or per channel over groups
+ *     of consecutive tokens, with a full-precision residual window of the most
+ *     recent keys (KIVI, as described in "Sub-8-Bit KV Cache Quantization ...",
+ *     FAQ and "What the low-bit numbers actually cost"; "KV Cache Quantization —
+ *     8-bit and 4-bit", "The outlier problem: keys have outlier channels" and
+ *     "Why keys and values want different treatment").
+ *   - Dense-and-sparse keys: the largest-magnitude entries of each key vector
+ *     kept in fp16 outside the dense codes (KVQuant, "Sub-8-Bit KV Cache
+ *     Quantization ...", "What the low-bit numbers actually cost").
+ *   - Decode attention that streams the packed cache and dequantizes on the
+ *     fly ("KV Cache Quantization — 8-bit and 4-bit", "Decode is memory-bound,
+ *     so smaller is also faster").
+ *
+ * Exact arithmetic of one quantization group (x_i are fp16 values widened to
+ * fp32; every operation is IEEE fp32 with round-to-nearest-even):
+ *   q_min = -2^(b-1), q_max = 2^(b-1) - 1, n_lev = q_max - q_min
+ *   x_min, x_max  = min / max of the group
+ *   if x_max > x_min:  s32 = (x_max - x_min) / (float)n_lev
+ *                      s16 = smallest fp16 >= s32 (round toward +inf)
+ *   else (constant):   s16 = |x_min| if x_min != 0, else 1.0
+ *   s  = (float)s16
+ *   z  = (float)q_min - rint(x_min / s), clamped to [-2048, 2048]; z16 = fp16(z)
+ *   q_i = clamp(rint(x_i / s) + z, q_min, q_max)       (rint: half to even)
+ *   stored code u_i = q_i - q_min  (unsigned, b bits)
+ *   x_hat_i = s * (q_i - z)   (exact in fp32)
+ * Divisions are true IEEE divisions, never multiplication by a reciprocal.
+ * Rounding the scale up keeps every in-range element within s/2 of its
+ * reconstruction, the bound the "Integer quantization in one screen" section
+ * states.
+ *
+ * Token state of one sequence (per KV head, identical for all heads)
+ *   L  = tokens held (device seq_len[b]; host copy len_host[b]).
+ *   Per-token keys:   all L tokens are quantized (Q = L).
+ *   Per-channel keys: Q = L - (L mod R) tokens are quantized in groups of
+ *                     G = 32 tokens aligned at multiples of 32 from token 0;
+ *                     the last r = L mod R keys stay fp16 in the residual
+ *                     window. Appending keys fills the window; when it holds R
+ *                     keys all R are quantized (R/32 groups) and it empties.
+ *   Values are always quantized per token on append.
+ *
+ * ---------------------------------------------------------------------------
+ * Memory layout (all arrays dense, little-endian, device memory, caller-owned;
+ * T = max_tokens, a multiple of 32; H = n_kv_heads; D = d_head = 128;
+ * kb / vb = key / value bits; "meta word" = uint32 (fp16 scale bits) |
+ * (fp16 zero bits) << 16):
+ *
+ *   k_codes  uint8 [B][H][T][D*kb/8]
+ *            token-major rows; channel c's code occupies bits
+ *            [(c*kb) mod 8, +kb) of byte (c*kb)/8 of its token row.
+ *   k_meta   per-token keys:   uint32 meta word [B][H][T]
+ *            per-channel keys: uint32 meta word [B][H][T/32][D]
+ *            (one word per (32-token group, channel)).
+ *   k_resid  per-channel keys only: fp16 [B][H][R][D]; slot j holds token
+ *            Q + j (j < r). Unused slots are not read.
+ *   k_sparse per-channel keys with k_sparse_per_vector == 2 only:
+ *            uint32 [B][H][T][2]: word 0 = fp16 value of entry 0 | fp16 value
+ *            of entry 1 << 16; word 1 = channel of entry 0 | channel of entry
+ *            1 << 16. A row-regular CSR: every quantized token has exactly two
+ *            entries, so the row pointer of token t is implicitly 2*t.
+ *            Entries are ordered by ascending channel.
+ *   v_codes  uint8 [B][H][T/32][D][4*vb]
+ *            per 32-token block, one record of 32 codes per channel; token
+ *            tau (0..31 within the block) occupies bits [(tau*vb) mod 8, +vb)
+ *            of byte (tau*vb)/8 of the record.
+ *   v_meta   uint32 meta word [B][H][T]
+ *   seq_len  int32 [B]
+ * Code bits of token slots >= L inside a byte written by the library are 0.
+ * Buffers must be zero-filled before the first append of a sequence.
+ *
+ * Fresh input tensors
+ *   k_new, v_new: fp16 [N][H][D], the new tokens of all sequences packed back
+ *   to back; sequence b owns rows cu_new[b] .. cu_new[b+1]-1 (cu_new int32
+ *   [B+1] on the device, cu_new[0] = 0) and n_new_host[b] = cu_new[b+1] -
+ *   cu_new[b] on the host.
+ *   q:   fp16 [B][Hq][D];  out: fp32 [B][Hq][D].
+ *   Query head h attends with KV head h / (Hq / H) (consecutive grouping).
+ *   Base pointers must be 256-byte aligned.
+ *
+ * Ownership and concurrency
+ *   The library never allocates, frees, or synchronizes; every kernel is
+ *   enqueued on the caller's stream and returns at once. It keeps no state
+ *   between calls. Calls that touch the same cache must be ordered by the
+ *   caller (same stream). Asynchronous device faults surface at the caller's
+ *   next synchronization.
+ *
+ * Errors
+ *   Arguments are validated on the host before anything is launched; an error
+ *   status means nothing was enqueued and no host state changed. KVQ_EHIP is
+ *   returned when a launch fails (hipGetLastError).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_EINVAL = 1,        /* a null pointer, a bad size or a bad alignment   */
+  KVQ_EUNSUPPORTED = 2,  /* a configuration this build does not implement   */
+  KVQ_ECAPACITY = 3,     /* an append would exceed max_tokens               */
+  KVQ_EWORKSPACE = 4,    /* workspace smaller than kvq_workspace_bytes      */
+  KVQ_EHIP = 5           /* a HIP launch failed                             */
+} kvq_status;
+
+enum { KVQ_AXIS_TOKEN = 0, KVQ_AXIS_CHANNEL = 1 };
+
+/* Quantization configuration, passed by value through a host pointer. */
+typedef struct kvq_config {
+  int32_t d_head;              /* channels per head; 128 is supported        */
+  int32_t n_kv_heads;          /* H >= 1                                     */
+  int32_t n_q_heads;           /* Hq, a multiple of H with Hq/H in {1,2,4,8} */
+  int32_t k_bits;              /* 8, 4 or 2                                  */
+  int32_t v_bits;              /* 8, 4 or 2                                  */
+  int32_t k_axis;              /* KVQ_AXIS_TOKEN or KVQ_AXIS_CHANNEL         */
+  int32_t k_group_tokens;      /* G: 32 for channel axis, 0 for token axis   */
+  int32_t k_residual_tokens;   /* R: a positive multiple of 32 for channel
+                                  axis, 0 for token axis                     */
+  int32_t v_group_channels;    /* channels per value group; must be d_head   */
+  int32_t k_sparse_per_vector; /* 0, or 2 (channel axis only)                */
+} kvq_config;
+
+/* Host-side descriptor of one cache; pointers name device memory except
+ * len_host. All pointers are owned by the caller. */
+typedef struct kvq_cache {
+  int32_t batch;        /* B                                                 */
+  int32_t max_tokens;   /* T, capacity per sequence, a multiple of 32        */
+  void* k_codes;
+  void* k_meta;
+  void* k_resid;        /* NULL unless k_axis == KVQ_AXIS_CHANNEL            */
+  void* k_sparse;       /* NULL unless k_sparse_per_vector > 0               */
+  void* v_codes;
+  void* v_meta;
+  int32_t* seq_len;     /* device int32 [B]                                  */
+  int32_t* len_host;    /* host int32 [B], kept equal to seq_len by appends  */
+} kvq_cache;
+
+/* Byte sizes of every cache array for (cfg, batch, max_tokens), plus the
+ * nominal size 2*H*D*T*bits/8*B from the bytes-per-token formula ("KV Cache
+ * Quantization — 8-bit and 4-bit", "The bytes-per-token formula" and "A worked
+ * memory example", one layer) and the cache's actual total. */
+typedef struct kvq_sizes {
+  uint64_t k_codes, k_meta, k_resid, k_sparse, v_codes, v_meta, seq_len;
+  uint64_t nominal_bytes;  /* codes only, no scales, per the formula        */
+  uint64_t total_bytes;    /* sum of every array above                      */
+} kvq_sizes;
+
+/* Fills *out_host. KVQ_EINVAL / KVQ_EUNSUPPORTED on a bad configuration or
+ * size. Pure host function. */
+kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch,
+                           int32_t max_tokens, kvq_sizes* out_host);
+
+/* Bytes of device workspace kvq_decode_attention needs for this shape
+ * (split-K partial results). 0 on a bad configuration. Pure host function. */
+size_t kvq_workspace_bytes(const kvq_config* cfg, int32_t batch,
+                           int32_t max_tokens);
+
+/* Quantize-on-append. Appends n_new_host[b] tokens of keys and values to
+ * sequence b, quantizing per the group arithmetic above: values per token;
+ * keys per token, or into the residual window with a flush of R keys as R/32
+ * per-channel groups whenever the window fills. With k_sparse_per_vector == 2
+ * each key vector being flushed first gives up its two largest-|x| entries
+ * (ties to the lower channel) to k_sparse and has them set to +0 before the
+ * group statistics. Updates seq_len on the device and len_host on the host.
+ * Errors: KVQ_EINVAL (null pointer, negative count, misaligned base),
+ * KVQ_EUNSUPPORTED, KVQ_ECAPACITY (len_host[b] + n_new_host[b] > max_tokens),
+ * KVQ_EHIP. */
+kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache,
+                      const void* k_new, const void* v_new,
+                      const int32_t* cu_new_dev, const int32_t* n_new_host,
+                      void* stream /* hipStream_t */);
+
+/* Decode attention for one new query token per sequence:
+ *   out[b][h] = sum_t softmax_t(softmax_scale * q[b][h] . K_hat[b][kv][t])
+ *               * V_hat[b][kv][t],   kv = h / (Hq / H), t < seq_len[b],
+ * where K_hat / V_hat are the dequantized codes (plus sparse entries), and
+ * residual keys are the stored fp16 values. A sequence with no tokens gets
+ * out = 0. ws is device workspace of at least kvq_workspace_bytes(cfg,
+ * cache->batch, cache->max_tokens) bytes; its contents need no initial value.
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EWORKSPACE, KVQ_EHIP. */
+kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
+                                const void* q, float* out, float softmax_scale,
+                                void* ws, size_t ws_bytes,
+                                void* stream /* hipStream_t */);
+
+/* Writes the dequantized cache as fp16 [B][T][H][D]: K_hat = fp16(s*(q - z))
+ * plus sparse entries for quantized keys, the stored fp16 value for residual
+ * keys, V_hat = fp16(s*(q - z)); token slots t >= seq_len[b] are written as
+ * +0. The fp16 conversions round to nearest even. This is the separate
+ * materializing pass the attention path avoids; it exists for checking and
+ * for callers that need plain fp16 tensors.
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EHIP. */
+kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache,
+                          void* k_out, void* v_out,
+                          void* stream /* hipStream_t */);
+
+/* Static text for a status code. */
+const char* kvq_status_string(kvq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */
