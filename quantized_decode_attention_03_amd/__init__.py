@@ -1,7 +1,135 @@
 """Low-bit KV-cache quantization and fused-dequant decode attention for MI355X.
 
 The work runs in hand-written HIP kernels (gfx950) behind the C ABI declared in
-include/kvq.h; this package is a thin ctypes binding over that library plus the
-seeded synthetic workloads. Importing it loads nothing; the native library is
-loaded on first use and its absence is an error (there is no CPU fallback).
+include/kvq.h; this module is a thin binding with the same entry names
+(argument marshalling only). PyTorch supplies device memory and streams.
+Importing the package loads nothing; the native library is loaded on first use
+and its absence is an error (there is no CPU fallback).
 """
+import ctypes
+
+from . import _native as N
+
+__all__ = ["Config", "KVCache", "kvq_cache_sizes", "kvq_workspace_bytes", "kvq_append",
+           "kvq_decode_attention", "kvq_dequantize", "KVQError"]
+
+KVQError = N.KVQError
+
+
+class Config:
+    """Mirror of kvq_config. k_axis is "token" or "channel"."""
+
+    def __init__(self, n_kv_heads, n_q_heads, k_bits, v_bits, k_axis="token",
+                 k_group_tokens=0, k_residual_tokens=0, k_sparse_per_vector=0, d_head=128):
+        self.d_head = d_head
+        self.n_kv_heads = n_kv_heads
+        self.n_q_heads = n_q_heads
+        self.k_bits = k_bits
+        self.v_bits = v_bits
+        self.k_axis = k_axis
+        self.k_group_tokens = k_group_tokens
+        self.k_residual_tokens = k_residual_tokens
+        self.k_sparse_per_vector = k_sparse_per_vector
+
+    @classmethod
+    def from_spec(cls, s):
+        return cls(s.n_kv_heads, s.n_q_heads, s.k_bits, s.v_bits, s.k_axis, s.k_group,
+                   s.k_residual, s.k_sparse, s.d_head)
+
+    def c(self):
+        return N.kvq_config(self.d_head, self.n_kv_heads, self.n_q_heads, self.k_bits,
+                            self.v_bits,
+                            N.KVQ_AXIS_CHANNEL if self.k_axis == "channel" else N.KVQ_AXIS_TOKEN,
+                            self.k_group_tokens, self.k_residual_tokens, self.d_head,
+                            self.k_sparse_per_vector)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def kvq_cache_sizes(cfg, batch, max_tokens):
+    out = N.kvq_sizes()
+    c = cfg.c()
+    N.check(N.lib().kvq_cache_sizes(ctypes.byref(c), batch, max_tokens, ctypes.byref(out)),
+            "kvq_cache_sizes")
+    return {f: getattr(out, f) for f, _ in N.kvq_sizes._fields_}
+
+
+def kvq_workspace_bytes(cfg, batch, max_tokens):
+    c = cfg.c()
+    return int(N.lib().kvq_workspace_bytes(ctypes.byref(c), batch, max_tokens))
+
+
+class KVCache:
+    """One layer's packed cache in caller-owned (torch) device memory, laid out
+    as include/kvq.h documents. Buffers start zero-filled."""
+
+    def __init__(self, cfg, batch, max_tokens, device="cuda"):
+        import torch
+        self.cfg, self.batch, self.max_tokens = cfg, batch, max_tokens
+        sz = kvq_cache_sizes(cfg, batch, max_tokens)
+        self.sizes = sz
+
+        def buf(n):
+            return torch.zeros(max(int(n), 1), dtype=torch.uint8, device=device) if n else None
+
+        self.k_codes = buf(sz["k_codes"])
+        self.k_meta = buf(sz["k_meta"])
+        self.k_resid = buf(sz["k_resid"])
+        self.k_sparse = buf(sz["k_sparse"])
+        self.v_codes = buf(sz["v_codes"])
+        self.v_meta = buf(sz["v_meta"])
+        self.seq_len = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.len_host = (ctypes.c_int32 * batch)()
+        self._c = N.kvq_cache(
+            batch, max_tokens, _ptr(self.k_codes), _ptr(self.k_meta), _ptr(self.k_resid),
+            _ptr(self.k_sparse), _ptr(self.v_codes), _ptr(self.v_meta),
+            ctypes.cast(ctypes.c_void_p(self.seq_len.data_ptr()), ctypes.POINTER(ctypes.c_int32)),
+            ctypes.cast(self.len_host, ctypes.POINTER(ctypes.c_int32)))
+        self._cfg = cfg.c()
+
+    def lengths(self):
+        return list(self.len_host)
+
+    def copy_from(self, other):
+        """Copy the whole state of another cache of the same shape (device
+        buffers and host lengths)."""
+        for name in ("k_codes", "k_meta", "k_resid", "k_sparse", "v_codes", "v_meta", "seq_len"):
+            a, b = getattr(self, name), getattr(other, name)
+            if a is not None:
+                a.copy_(b)
+        for i in range(self.batch):
+            self.len_host[i] = other.len_host[i]
+
+
+def kvq_append(cache, k_new, v_new, cu_new, n_new, stream=None):
+    """k_new, v_new: fp16 device tensors [N, H, D]; cu_new: int32 device
+    tensor [B+1]; n_new: host sequence of B ints."""
+    n = (ctypes.c_int32 * cache.batch)(*[int(x) for x in n_new])
+    N.check(N.lib().kvq_append(ctypes.byref(cache._cfg), ctypes.byref(cache._c), _ptr(k_new),
+                               _ptr(v_new),
+                               ctypes.cast(ctypes.c_void_p(cu_new.data_ptr()),
+                                           ctypes.POINTER(ctypes.c_int32)),
+                               n, _stream(stream)), "kvq_append")
+
+
+def kvq_decode_attention(cache, q, out, softmax_scale, ws, stream=None):
+    """q: fp16 [B, Hq, D]; out: fp32 [B, Hq, D]; ws: device buffer of at least
+    kvq_workspace_bytes bytes."""
+    N.check(N.lib().kvq_decode_attention(ctypes.byref(cache._cfg), ctypes.byref(cache._c),
+                                         _ptr(q), _ptr(out), ctypes.c_float(softmax_scale),
+                                         _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()),
+                                         _stream(stream)), "kvq_decode_attention")
+
+
+def kvq_dequantize(cache, k_out, v_out, stream=None):
+    """k_out, v_out: fp16 device tensors [B, T, H, D]."""
+    N.check(N.lib().kvq_dequantize(ctypes.byref(cache._cfg), ctypes.byref(cache._c), _ptr(k_out),
+                                   _ptr(v_out), _stream(stream)), "kvq_dequantize")

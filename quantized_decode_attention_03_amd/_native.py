@@ -1,0 +1,81 @@
+"""ctypes declarations of the C ABI in include/kvq.h and the library loader.
+
+The library is libkvq.so next to this file (built by ``build.py``). A missing
+library is an error: nothing here computes anything.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvq.so")
+
+KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EHIP = range(6)
+KVQ_AXIS_TOKEN, KVQ_AXIS_CHANNEL = 0, 1
+
+EXPORTS = ("kvq_cache_sizes", "kvq_workspace_bytes", "kvq_append", "kvq_decode_attention",
+           "kvq_dequantize", "kvq_status_string")
+
+
+class kvq_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "d_head", "n_kv_heads", "n_q_heads", "k_bits", "v_bits", "k_axis", "k_group_tokens",
+        "k_residual_tokens", "v_group_channels", "k_sparse_per_vector")]
+
+
+class kvq_cache(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("k_codes", ctypes.c_void_p), ("k_meta", ctypes.c_void_p),
+                ("k_resid", ctypes.c_void_p), ("k_sparse", ctypes.c_void_p),
+                ("v_codes", ctypes.c_void_p), ("v_meta", ctypes.c_void_p),
+                ("seq_len", ctypes.POINTER(ctypes.c_int32)),
+                ("len_host", ctypes.POINTER(ctypes.c_int32))]
+
+
+class kvq_sizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in (
+        "k_codes", "k_meta", "k_resid", "k_sparse", "v_codes", "v_meta", "seq_len",
+        "nominal_bytes", "total_bytes")]
+
+
+_lib = None
+
+
+class KVQError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def lib():
+    """Load libkvq.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m quantized_decode_attention_03_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        cp, vp, i32, i32p = ctypes.POINTER, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)
+        L.kvq_cache_sizes.argtypes = [cp(kvq_config), i32, i32, cp(kvq_sizes)]
+        L.kvq_cache_sizes.restype = ctypes.c_int
+        L.kvq_workspace_bytes.argtypes = [cp(kvq_config), i32, i32]
+        L.kvq_workspace_bytes.restype = ctypes.c_size_t
+        L.kvq_append.argtypes = [cp(kvq_config), cp(kvq_cache), vp, vp, i32p, i32p, vp]
+        L.kvq_append.restype = ctypes.c_int
+        L.kvq_decode_attention.argtypes = [cp(kvq_config), cp(kvq_cache), vp, vp, ctypes.c_float,
+                                           vp, ctypes.c_size_t, vp]
+        L.kvq_decode_attention.restype = ctypes.c_int
+        L.kvq_dequantize.argtypes = [cp(kvq_config), cp(kvq_cache), vp, vp, vp]
+        L.kvq_dequantize.restype = ctypes.c_int
+        L.kvq_status_string.argtypes = [ctypes.c_int]
+        L.kvq_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(s):
+    return lib().kvq_status_string(s).decode()
+
+
+def check(status, what):
+    if status != KVQ_OK:
+        raise KVQError(status, what)

@@ -1,0 +1,220 @@
+// C-ABI entry points of the kvq library: argument validation on the host,
+// then kernel launches on the caller's stream. No allocation, no
+// synchronization (except under KVQ_DEBUG=1), no state kept between calls.
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+bool debug_sync() {
+  static const int on = [] {
+    const char* e = getenv("KVQ_DEBUG");
+    return (e && e[0] == '1') ? 1 : 0;
+  }();
+  return on != 0;
+}
+
+kvq_status after_launch(hipError_t e, hipStream_t st) {
+  if (e != hipSuccess) return KVQ_EHIP;
+  if (debug_sync()) {
+    if (hipStreamSynchronize(st) != hipSuccess) return KVQ_EHIP;
+    if (hipGetLastError() != hipSuccess) return KVQ_EHIP;
+  }
+  return KVQ_OK;
+}
+
+bool bits_ok(int b) { return b == 2 || b == 4 || b == 8; }
+
+kvq_status check_config(const kvq_config* cfg) {
+  if (!cfg) return KVQ_EINVAL;
+  if (cfg->n_kv_heads < 1 || cfg->n_q_heads < 1) return KVQ_EINVAL;
+  if (cfg->n_q_heads % cfg->n_kv_heads != 0) return KVQ_EINVAL;
+  const int g = cfg->n_q_heads / cfg->n_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return KVQ_EUNSUPPORTED;
+  if (cfg->d_head != kD) return KVQ_EUNSUPPORTED;
+  if (cfg->v_group_channels != cfg->d_head) return KVQ_EUNSUPPORTED;
+  if (!bits_ok(cfg->k_bits) || !bits_ok(cfg->v_bits)) return KVQ_EUNSUPPORTED;
+  if (cfg->k_axis == KVQ_AXIS_TOKEN) {
+    if (cfg->k_group_tokens != 0 || cfg->k_residual_tokens != 0) return KVQ_EINVAL;
+    if (cfg->k_sparse_per_vector != 0) return KVQ_EUNSUPPORTED;
+  } else if (cfg->k_axis == KVQ_AXIS_CHANNEL) {
+    if (cfg->k_group_tokens != kBlock) return KVQ_EUNSUPPORTED;
+    if (cfg->k_residual_tokens <= 0 || cfg->k_residual_tokens % kBlock != 0) return KVQ_EINVAL;
+    if (cfg->k_sparse_per_vector != 0 && cfg->k_sparse_per_vector != 2) return KVQ_EUNSUPPORTED;
+  } else {
+    return KVQ_EINVAL;
+  }
+  return KVQ_OK;
+}
+
+kvq_status check_shape(int32_t batch, int32_t max_tokens) {
+  if (batch < 1 || max_tokens < kBlock || max_tokens % kBlock != 0) return KVQ_EINVAL;
+  if (max_tokens > (1 << 24)) return KVQ_EUNSUPPORTED;
+  return KVQ_OK;
+}
+
+bool aligned(const void* p) { return ((uintptr_t)p & 255u) == 0; }
+
+kvq_status check_cache(const kvq_config* cfg, const kvq_cache* c) {
+  if (!c) return KVQ_EINVAL;
+  kvq_status s = check_shape(c->batch, c->max_tokens);
+  if (s != KVQ_OK) return s;
+  const void* req[] = {c->k_codes, c->k_meta, c->v_codes, c->v_meta, c->seq_len};
+  for (const void* p : req)
+    if (!p || !aligned(p)) return KVQ_EINVAL;
+  if (!c->len_host) return KVQ_EINVAL;
+  if (cfg->k_axis == KVQ_AXIS_CHANNEL && (!c->k_resid || !aligned(c->k_resid))) return KVQ_EINVAL;
+  if (cfg->k_sparse_per_vector && (!c->k_sparse || !aligned(c->k_sparse))) return KVQ_EINVAL;
+  for (int b = 0; b < c->batch; ++b)
+    if (c->len_host[b] < 0 || c->len_host[b] > c->max_tokens) return KVQ_EINVAL;
+  return KVQ_OK;
+}
+
+CacheView view_of(const kvq_config* cfg, const kvq_cache* c) {
+  CacheView v;
+  v.B = c->batch;
+  v.H = cfg->n_kv_heads;
+  v.T = c->max_tokens;
+  v.kbits = cfg->k_bits;
+  v.vbits = cfg->v_bits;
+  v.kaxis = cfg->k_axis == KVQ_AXIS_CHANNEL ? 1 : 0;
+  v.R = cfg->k_residual_tokens;
+  v.sparse = cfg->k_sparse_per_vector;
+  v.k_codes = (uint8_t*)c->k_codes;
+  v.k_meta = (uint32_t*)c->k_meta;
+  v.k_resid = (uint16_t*)c->k_resid;
+  v.k_sparse = (uint32_t*)c->k_sparse;
+  v.v_codes = (uint8_t*)c->v_codes;
+  v.v_meta = (uint32_t*)c->v_meta;
+  v.seq_len = c->seq_len;
+  return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_EINVAL: return "invalid argument";
+    case KVQ_EUNSUPPORTED: return "unsupported configuration";
+    case KVQ_ECAPACITY: return "append exceeds cache capacity";
+    case KVQ_EWORKSPACE: return "workspace too small";
+    case KVQ_EHIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch, int32_t max_tokens,
+                           kvq_sizes* out) {
+  kvq_status s = check_config(cfg);
+  if (s != KVQ_OK) return s;
+  if ((s = check_shape(batch, max_tokens)) != KVQ_OK) return s;
+  if (!out) return KVQ_EINVAL;
+  const uint64_t n = (uint64_t)batch * cfg->n_kv_heads, T = (uint64_t)max_tokens, D = kD;
+  memset(out, 0, sizeof(*out));
+  out->k_codes = n * T * D * cfg->k_bits / 8;
+  out->v_codes = n * T * D * cfg->v_bits / 8;
+  out->v_meta = n * T * 4;
+  out->seq_len = (uint64_t)batch * 4;
+  if (cfg->k_axis == KVQ_AXIS_CHANNEL) {
+    out->k_meta = n * (T / kBlock) * D * 4;
+    out->k_resid = n * (uint64_t)cfg->k_residual_tokens * D * 2;
+    out->k_sparse = cfg->k_sparse_per_vector ? n * T * 8 : 0;
+  } else {
+    out->k_meta = n * T * 4;
+  }
+  out->nominal_bytes = n * T * D * (cfg->k_bits + cfg->v_bits) / 8;
+  out->total_bytes = out->k_codes + out->k_meta + out->k_resid + out->k_sparse + out->v_codes +
+                     out->v_meta + out->seq_len;
+  return KVQ_OK;
+}
+
+size_t kvq_workspace_bytes(const kvq_config* cfg, int32_t batch, int32_t max_tokens) {
+  if (check_config(cfg) != KVQ_OK || check_shape(batch, max_tokens) != KVQ_OK) return 0;
+  return (size_t)batch * cfg->n_q_heads * max_splits_for(max_tokens) * kPartialFloats * sizeof(float);
+}
+
+kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new, const void* v_new,
+                      const int32_t* cu_new_dev, const int32_t* n_new_host, void* stream) {
+  kvq_status s = check_config(cfg);
+  if (s != KVQ_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVQ_OK) return s;
+  if (!cu_new_dev || !n_new_host) return KVQ_EINVAL;
+  int64_t total = 0;
+  int max_tok_blocks = 0, max_flush_blocks = 0;
+  const int R = cfg->k_residual_tokens;
+  for (int b = 0; b < cache->batch; ++b) {
+    const int n = n_new_host[b];
+    if (n < 0) return KVQ_EINVAL;
+    const int L = cache->len_host[b];
+    if ((int64_t)L + n > cache->max_tokens) return KVQ_ECAPACITY;
+    total += n;
+    if (n == 0) continue;
+    const int L2 = L + n;
+    max_tok_blocks = std::max(max_tok_blocks, (L2 - 1) / kBlock - L / kBlock + 1);
+    if (cfg->k_axis == KVQ_AXIS_CHANNEL) {
+      const int Q = L - L % R, Q2 = L2 - L2 % R;
+      max_flush_blocks = std::max(max_flush_blocks, (Q2 - Q) / kBlock);
+    }
+  }
+  if (total == 0) return KVQ_OK;
+  if (!k_new || !v_new || !aligned(k_new) || !aligned(v_new)) return KVQ_EINVAL;
+  const CacheView v = view_of(cfg, cache);
+  const AppendInputs in{(const uint16_t*)k_new, (const uint16_t*)v_new, cu_new_dev};
+  hipStream_t st = (hipStream_t)stream;
+  if (max_flush_blocks > 0) {
+    if ((s = after_launch(launch_flush_keys(v, in, max_flush_blocks, st), st)) != KVQ_OK) return s;
+  }
+  if ((s = after_launch(launch_append_tokens(v, in, max_tok_blocks, st), st)) != KVQ_OK) return s;
+  if ((s = after_launch(launch_update_lengths(v, cu_new_dev, st), st)) != KVQ_OK) return s;
+  for (int b = 0; b < cache->batch; ++b) cache->len_host[b] += n_new_host[b];
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                                float* out, float softmax_scale, void* ws, size_t ws_bytes,
+                                void* stream) {
+  kvq_status s = check_config(cfg);
+  if (s != KVQ_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVQ_OK) return s;
+  if (!q || !out || !ws || !aligned(q) || !aligned(out) || !aligned(ws)) return KVQ_EINVAL;
+  if (ws_bytes < kvq_workspace_bytes(cfg, cache->batch, cache->max_tokens)) return KVQ_EWORKSPACE;
+  int lmax = 0;
+  for (int b = 0; b < cache->batch; ++b) lmax = std::max(lmax, (int)cache->len_host[b]);
+  AttnPlan p;
+  p.Hq = cfg->n_q_heads;
+  p.group = cfg->n_q_heads / cfg->n_kv_heads;
+  p.scale = softmax_scale;
+  const int tiles = std::max(1, (lmax + kBlock - 1) / kBlock);
+  const int pairs = cache->batch * cfg->n_kv_heads;
+  int ns = std::max(1, (2048 + pairs - 1) / pairs);
+  ns = std::min(ns, std::min(tiles, max_splits_for(cache->max_tokens)));
+  const int tiles_per = (tiles + ns - 1) / ns;
+  p.tokens_per_split = tiles_per * kBlock;
+  p.n_split = (tiles + tiles_per - 1) / tiles_per;
+  const CacheView v = view_of(cfg, cache);
+  hipStream_t st = (hipStream_t)stream;
+  return after_launch(launch_decode_attention(v, p, (const uint16_t*)q, out, (float*)ws, st), st);
+}
+
+kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache, void* k_out, void* v_out,
+                          void* stream) {
+  kvq_status s = check_config(cfg);
+  if (s != KVQ_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVQ_OK) return s;
+  if (!k_out || !v_out || !aligned(k_out) || !aligned(v_out)) return KVQ_EINVAL;
+  const CacheView v = view_of(cfg, cache);
+  hipStream_t st = (hipStream_t)stream;
+  return after_launch(launch_dequantize(v, (uint16_t*)k_out, (uint16_t*)v_out, st), st);
+}
+
+}  // extern "C"

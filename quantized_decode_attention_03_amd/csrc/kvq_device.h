@@ -1,0 +1,82 @@
+// Device-side helpers shared by the kvq kernels (gfx950).
+//
+// The group arithmetic follows "KV Cache Quantization — 8-bit and 4-bit",
+// section "Integer quantization in one screen": scale = (x_max - x_min) /
+// (q_max - q_min), zero_point = q_min - round(x_min / scale), q = round(x /
+// scale) + zero_point, x_hat = scale * (q - zero_point). Every step is an IEEE
+// fp32 operation with round-to-nearest-even; the fp16 scale is rounded toward
+// +inf so the reconstruction error stays within scale/2. Divisions are true
+// divisions (the library is built with correctly rounded fp32 division).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+__device__ __forceinline__ float h2f(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+__device__ __forceinline__ uint16_t f2h_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+// Smallest fp16 >= f for finite f >= 0.
+__device__ __forceinline__ uint16_t f2h_up(float f) {
+  uint16_t b = f2h_rne(f);
+  if (h2f(b) < f) b += 1;
+  return b;
+}
+
+__host__ __device__ constexpr int qmin_of(int bits) { return -(1 << (bits - 1)); }
+__host__ __device__ constexpr int qmax_of(int bits) { return (1 << (bits - 1)) - 1; }
+
+struct GroupQ {
+  float s;      // scale as fp32 (exactly the stored fp16)
+  float z;      // zero-point as fp32 (an integer in [-2048, 2048])
+  uint32_t meta;  // fp16 scale bits | fp16 zero bits << 16
+};
+
+// Scale and zero-point of a group from its fp32 extremes.
+__device__ __forceinline__ GroupQ group_params(float xmin, float xmax, int bits) {
+#pragma clang fp contract(off)
+  const float nlev = (float)(qmax_of(bits) - qmin_of(bits));
+  uint16_t s16;
+  if (xmax > xmin) {
+    s16 = f2h_up((xmax - xmin) / nlev);
+  } else {
+    s16 = (xmin != 0.0f) ? f2h_rne(__builtin_fabsf(xmin)) : (uint16_t)0x3C00;
+  }
+  GroupQ g;
+  g.s = h2f(s16);
+  float z = (float)qmin_of(bits) - __builtin_rintf(xmin / g.s);
+  z = __builtin_fminf(__builtin_fmaxf(z, -2048.0f), 2048.0f);
+  g.z = z;
+  g.meta = (uint32_t)s16 | ((uint32_t)f2h_rne(z) << 16);
+  return g;
+}
+
+// Stored unsigned code u = q - q_min of one element.
+__device__ __forceinline__ uint32_t quant_code(float x, const GroupQ& g, int bits) {
+#pragma clang fp contract(off)
+  float q = __builtin_rintf(x / g.s) + g.z;
+  q = __builtin_fminf(__builtin_fmaxf(q, (float)qmin_of(bits)), (float)qmax_of(bits));
+  return (uint32_t)((int)q - qmin_of(bits));
+}
+
+// Exact fp32 reconstruction s * (q - z) from a stored code and a meta word.
+__device__ __forceinline__ float dequant(uint32_t u, uint32_t meta, int bits) {
+#pragma clang fp contract(off)
+  const float s = h2f((uint16_t)(meta & 0xFFFFu));
+  const float z = h2f((uint16_t)(meta >> 16));
+  return s * ((float)((int)u + qmin_of(bits)) - z);
+}
+
+// b-bit field i of a little-endian packed byte array.
+__device__ __forceinline__ uint32_t get_field(const uint8_t* p, int i, int bits) {
+  const int bit = i * bits;
+  return (p[bit >> 3] >> (bit & 7)) & ((1u << bits) - 1u);
+}
+
+}  // namespace kvq

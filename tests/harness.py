@@ -1,0 +1,124 @@
+"""Shared helpers of the GPU tests: run the same seeded inputs through the HIP
+library (via the C ABI) and through the oracle, and compare."""
+import math
+
+import numpy as np
+
+from oracle.cache import Config as RefConfig, RefCache
+from oracle import quant
+from quantized_decode_attention_03_amd import workloads as W
+
+ATOL = 2e-3   # attention tolerance, max-abs against the float64 oracle
+
+
+def ref_config(s):
+    return RefConfig(s.d_head, s.n_kv_heads, s.n_q_heads, s.k_bits, s.v_bits, s.k_axis,
+                     s.k_group, s.k_residual, s.k_sparse)
+
+
+def to_dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def cu_of(n):
+    import torch
+    cu = np.zeros(len(n) + 1, np.int32)
+    cu[1:] = np.cumsum(n)
+    return torch.from_numpy(cu).cuda()
+
+
+class Pair:
+    """A GPU cache and an oracle cache fed identical appends."""
+
+    def __init__(self, s, max_tokens, with_ref=True):
+        import quantized_decode_attention_03_amd as K
+        self.K = K
+        self.s = s
+        self.B = s.batch
+        self.gpu = K.KVCache(K.Config.from_spec(s), s.batch, max_tokens)
+        self.ref = RefCache(ref_config(s), s.batch, max_tokens) if with_ref else None
+        self.T = max_tokens
+
+    def append(self, k, v, n):
+        """k, v: fp16 numpy [N, H, D] packed by sequence."""
+        import torch
+        kd, vd = to_dev(k), to_dev(v)
+        self.K.kvq_append(self.gpu, kd, vd, cu_of(n), n)
+        if self.ref is not None:
+            self.ref.append(k, v, n)
+        torch.cuda.synchronize()
+
+    def attend(self, q, scale=None):
+        import torch
+        s = self.s
+        scale = 1.0 / math.sqrt(s.d_head) if scale is None else scale
+        out = torch.empty((self.B, s.n_q_heads, s.d_head), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(1, self.K.kvq_workspace_bytes(self.gpu.cfg, self.B, self.T)),
+                         dtype=torch.uint8, device="cuda")
+        self.K.kvq_decode_attention(self.gpu, to_dev(q), out, scale, ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), scale
+
+    def dequantize(self):
+        import torch
+        s = self.s
+        shape = (self.B, self.T, s.n_kv_heads, s.d_head)
+        k = torch.empty(shape, dtype=torch.float16, device="cuda")
+        v = torch.empty(shape, dtype=torch.float16, device="cuda")
+        self.K.kvq_dequantize(self.gpu, k, v)
+        torch.cuda.synchronize()
+        return k.cpu().numpy(), v.cpu().numpy()
+
+    def packed_gpu(self):
+        """Device buffers reshaped to the layout include/kvq.h documents."""
+        s, B, T, H, D = self.s, self.B, self.T, self.s.n_kv_heads, self.s.d_head
+        g = self.gpu
+        out = {
+            "k_codes": g.k_codes.cpu().numpy().reshape(B, H, T, D * s.k_bits // 8),
+            "v_codes": g.v_codes.cpu().numpy().reshape(B, H, T // 32, D, 4 * s.v_bits),
+            "v_meta": g.v_meta.cpu().numpy().view(np.uint32).reshape(B, H, T),
+        }
+        if s.k_axis == "channel":
+            out["k_meta"] = g.k_meta.cpu().numpy().view(np.uint32).reshape(B, H, T // 32, D)
+            out["k_resid"] = g.k_resid.cpu().numpy().view(np.uint16).reshape(B, H, s.k_residual, D)
+            if s.k_sparse:
+                out["k_sparse"] = g.k_sparse.cpu().numpy().view(np.uint32).reshape(B, H, T, 2)
+        else:
+            out["k_meta"] = g.k_meta.cpu().numpy().view(np.uint32).reshape(B, H, T)
+        return out
+
+    def assert_state_equal(self):
+        """Codes, metadata, sparse entries and residual keys byte-equal."""
+        ref = self.ref.pack()
+        got = self.packed_gpu()
+        for key, want in ref.items():
+            if key == "k_resid":
+                for b in range(self.B):
+                    r = int(self.ref.length[b]) - self.ref.n_quantized(b)
+                    assert np.array_equal(got[key][b, :, :r], want[b, :, :r]), (key, b)
+            else:
+                if not np.array_equal(got[key], want):
+                    bad = np.argwhere(got[key] != want)
+                    raise AssertionError(f"{key}: {len(bad)} mismatching entries, first {bad[:5].tolist()}")
+        lens = self.gpu.seq_len.cpu().numpy()
+        assert np.array_equal(lens, self.ref.length.astype(np.int32))
+        assert list(self.gpu.len_host) == self.ref.length.tolist()
+
+
+def prefill_inputs(s, layer=0, lens=None):
+    lens = W.seq_lengths(s) if lens is None else lens
+    ks, vs = [], []
+    for b in range(s.batch):
+        k, v = W.prefill(s, layer, b, int(lens[b]))
+        ks.append(k)
+        vs.append(v)
+    return np.concatenate(ks), np.concatenate(vs), [int(x) for x in lens]
+
+
+def max_abs(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0
+
+
+def f16_equal(a, b):
+    return np.array_equal(quant.f16_bits(a), quant.f16_bits(b))
