@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Decode benchmark on one MI355X.
+
+One step = one pass of the hot path over one batch: quantize-on-append of one
+new key/value token per sequence (with the residual flush when a window fills)
+followed by fused-dequant decode attention for one query token per sequence.
+Inputs are resident in HBM before timing starts. Cache replicas are rotated so
+each step reads a cache that is not resident in the 256 MB last-level cache.
+
+Prints one JSON line: tokens/s (value), ms per step, and for the attention
+kernel a roofline entry (algorithmic bytes per launch / measured launch time
+against 8 TB/s HBM) plus the float64 oracle timed on the host as a reported
+baseline.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn tokens/s + achieved HBM GB/s (% of peak), int4/int2 KV, 1 MI355X"
+PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(s, lens):
+    """Bytes one attention launch must move: every held token's codes and
+    metadata (plus residual fp16 keys and sparse entries), the fp16 queries and
+    the fp32 outputs. Per (sequence, KV head) with L tokens of which Q are
+    quantized keys."""
+    H, D = s.n_kv_heads, s.d_head
+    tot = 0
+    for L in lens:
+        Q = L if s.k_axis == "token" else L - L % s.k_residual
+        k = Q * D * s.k_bits // 8
+        k += (Q // 32) * D * 4 if s.k_axis == "channel" else Q * 4
+        k += (L - Q) * D * 2
+        k += Q * 8 if s.k_sparse else 0
+        v = L * D * s.v_bits // 8 + L * 4
+        tot += H * (k + v)
+    tot += s.batch * s.n_q_heads * D * (2 + 4)
+    return tot
+
+
+def cpu_baseline(s, n_seq, steps):
+    """The oracle's decode step (append + float64 attention) on a subset of the
+    sequences, timed on the host. Returns (tokens/s, threads, description)."""
+    from dataclasses import replace
+    from threadpoolctl import threadpool_info
+    from oracle.cache import Config as RC, RefCache
+    from quantized_decode_attention_03_amd import workloads as W
+    sub = replace(s, batch=n_seq)
+    lens = [int(x) for x in W.seq_lengths(s)[:n_seq]]
+    ref = RefCache(RC(s.d_head, s.n_kv_heads, s.n_q_heads, s.k_bits, s.v_bits, s.k_axis,
+                      s.k_group, s.k_residual, s.k_sparse), n_seq,
+                   ((max(lens) + steps + 31) // 32) * 32)
+    ks, vs = zip(*[W.prefill(s, 0, b, lens[b]) for b in range(n_seq)])
+    ref.append(np.concatenate(ks), np.concatenate(vs), lens)
+    scale = 1.0 / math.sqrt(s.d_head)
+    inputs = [W.step(sub, 0, i) for i in range(steps)]
+    t0 = time.perf_counter()
+    for q, kn, vn in inputs:
+        ref.append(kn, vn, [1] * n_seq)
+        ref.attention(q, scale)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return n_seq * steps / dt, threads, dt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5")
+    ap.add_argument("--replicas", type=int, default=0, help="cache copies rotated (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=16)
+    ap.add_argument("--cpu-steps", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path shards by sequence or KV head with no communication, "
+              "so one GPU's throughput is the per-GPU figure)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_decode_attention_03_amd as K
+    from quantized_decode_attention_03_amd import workloads as W
+    from quantized_decode_attention_03_amd import _native
+
+    _native.lib()
+    s = W.spec(args.config)
+    if s.layers != 1:
+        raise SystemExit("bench.py times single-layer workloads")
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    lens0 = [int(x) for x in W.seq_lengths(s)]
+    cache_bytes = algorithmic_bytes(s, lens0)
+    nrep = args.replicas or max(1, min(16, math.ceil(1.25e9 / cache_bytes)))
+    total_steps = args.warmup + args.steps
+    per_rep = math.ceil(total_steps / nrep)
+    T = ((max(lens0) + per_rep + 31) // 32) * 32
+    cfg = K.Config.from_spec(s)
+
+    # prefill one cache, then clone it into the replicas
+    ks, vs = zip(*[W.prefill(s, 0, b, lens0[b]) for b in range(s.batch)])
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens0)]).astype(np.int32), device=dev)
+    base = K.KVCache(cfg, s.batch, T)
+    K.kvq_append(base, torch.from_numpy(np.concatenate(ks)).to(dev),
+                 torch.from_numpy(np.concatenate(vs)).to(dev), cu, lens0)
+    del ks, vs
+    reps = [base]
+    for _ in range(nrep - 1):
+        r = K.KVCache(cfg, s.batch, T)
+        r.copy_from(base)
+        reps.append(r)
+
+    # per-step inputs resident on the device
+    pool = 16
+    qs, kn, vn = [], [], []
+    for i in range(pool):
+        q, k, v = W.step(s, 0, i)
+        qs.append(torch.from_numpy(q).to(dev))
+        kn.append(torch.from_numpy(k).to(dev))
+        vn.append(torch.from_numpy(v).to(dev))
+    cu1 = torch.arange(s.batch + 1, dtype=torch.int32, device=dev)
+    ones = [1] * s.batch
+    out = torch.empty((s.batch, s.n_q_heads, s.d_head), dtype=torch.float32, device=dev)
+    ws = torch.zeros(K.kvq_workspace_bytes(cfg, s.batch, T), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(s.d_head)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def run(i, ev=None):
+        r = reps[i % nrep]
+        K.kvq_append(r, kn[i % pool], vn[i % pool], cu1, ones, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        K.kvq_decode_attention(r, qs[i % pool], out, scale, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    # lengths seen by the timed attention launches
+    lens_timed = []
+    step_lens = [list(r.len_host) for r in reps]
+    for i in range(args.warmup, total_steps):
+        rr = i % nrep
+        step_lens[rr] = [x + 1 for x in step_lens[rr]]
+        lens_timed.append(list(step_lens[rr]))
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        run(args.warmup + j, events[j])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = [a.elapsed_time(b) for a, b in events]
+    attn_avg_s = float(np.mean(attn_ms)) / 1e3
+    bytes_avg = float(np.mean([algorithmic_bytes(s, L) for L in lens_timed]))
+    achieved = bytes_avg / attn_avg_s / 1e9
+
+    ms_per_step = wall / args.steps * 1e3
+    value = s.batch * args.steps / wall
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"int{s.k_bits}/int{s.v_bits} codes, f32 math",
+        "data": "synthetic",
+        "config": {"workload": s.name, "batch": s.batch, "n_q_heads": s.n_q_heads,
+                   "n_kv_heads": s.n_kv_heads, "d_head": s.d_head, "seq_len": s.seq_len,
+                   "k_bits": s.k_bits, "v_bits": s.v_bits, "k_axis": s.k_axis,
+                   "k_group": s.k_group, "k_residual": s.k_residual, "k_sparse": s.k_sparse,
+                   "cache_replicas": nrep},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_GBS, "traffic": None,
+                     "kernel": "kvq_decode_attention (attention + split merge)",
+                     "avg_launch_us": attn_avg_s * 1e6,
+                     "p10_p90_us": [float(np.percentile(attn_ms, 10)) * 1e3,
+                                    float(np.percentile(attn_ms, 90)) * 1e3],
+                     "algorithmic_bytes_per_launch": bytes_avg},
+    }
+    if not args.no_cpu_baseline:
+        tps, threads, dt = cpu_baseline(s, min(args.cpu_seqs, s.batch), args.cpu_steps)
+        res["cpu_baseline"] = {
+            "value": tps, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{min(args.cpu_seqs, s.batch)} of {s.batch} sequences x {args.cpu_steps} "
+                      f"decode steps (append + float64 attention), {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -140,7 +140,9 @@ kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch, int32_t max_tok
 
 size_t kvq_workspace_bytes(const kvq_config* cfg, int32_t batch, int32_t max_tokens) {
   if (check_config(cfg) != KVQ_OK || check_shape(batch, max_tokens) != KVQ_OK) return 0;
-  return (size_t)batch * cfg->n_q_heads * max_splits_for(max_tokens) * kPartialFloats * sizeof(float);
+  return (kPartialOffsetFloats(batch, cfg->n_kv_heads) +
+          (size_t)batch * cfg->n_q_heads * max_splits_for(max_tokens) * kPartialFloats) *
+         sizeof(float);
 }
 
 kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new, const void* v_new,
@@ -189,18 +191,23 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   if (!q || !out || !ws || !aligned(q) || !aligned(out) || !aligned(ws)) return KVQ_EINVAL;
   if (ws_bytes < kvq_workspace_bytes(cfg, cache->batch, cache->max_tokens)) return KVQ_EWORKSPACE;
   int lmax = 0;
-  for (int b = 0; b < cache->batch; ++b) lmax = std::max(lmax, (int)cache->len_host[b]);
+  int64_t total = 0;
+  for (int b = 0; b < cache->batch; ++b) {
+    lmax = std::max(lmax, (int)cache->len_host[b]);
+    total += cache->len_host[b];
+  }
   AttnPlan p;
   p.Hq = cfg->n_q_heads;
   p.group = cfg->n_q_heads / cfg->n_kv_heads;
   p.scale = softmax_scale;
-  const int tiles = std::max(1, (lmax + kBlock - 1) / kBlock);
-  const int pairs = cache->batch * cfg->n_kv_heads;
-  int ns = std::max(1, (2048 + pairs - 1) / pairs);
-  ns = std::min(ns, std::min(tiles, max_splits_for(cache->max_tokens)));
-  const int tiles_per = (tiles + ns - 1) / ns;
-  p.tokens_per_split = tiles_per * kBlock;
-  p.n_split = (tiles + tiles_per - 1) / tiles_per;
+  // tokens per split: about 1024 workgroups over all (sequence, KV head)
+  // pairs, each at least 256 and at most 2048 tokens (bounds the imbalance of
+  // ragged lengths), a multiple of 32
+  int64_t per = (total * cfg->n_kv_heads + 1023) / 1024;
+  per = std::min<int64_t>(std::max<int64_t>(per, kMinSplitTokens), 2048);
+  per = (per + kBlock - 1) / kBlock * kBlock;
+  p.tokens_per_split = (int)per;
+  p.n_split = std::max(1, (int)((lmax + per - 1) / per));
   const CacheView v = view_of(cfg, cache);
   hipStream_t st = (hipStream_t)stream;
   return after_launch(launch_decode_attention(v, p, (const uint16_t*)q, out, (float*)ws, st), st);

@@ -1,4 +1,4 @@
-// Fused-dequant decode attention (gfx950).
+// Fused-dequant decode attention on the matrix cores (gfx950).
 //
 // Decode streams the whole cache once per token and is bound by memory
 // bandwidth, so the packed integer codes are read directly and dequantized in
@@ -9,211 +9,671 @@
 // sparse key entries ("Sub-8-Bit KV Cache Quantization Is Not a Free Lever for
 // an RDNA4 Agent Swarm", "The RDNA4 kernel angle").
 //
-// Work split: grid (split, KV head, sequence); each workgroup reduces a token
-// range with an online softmax and writes (m, l, o[128]) per query head; a
-// second kernel merges the splits with a log-sum-exp.
+// Shape of the work. The g query heads that share a KV head turn both products
+// into small dense contractions, so they run on v_mfma_f32_16x16x32_f16:
+//   S^T[token, col] = sum_c A[token, c] * B[c, col]
+//       A = dequantization-ready key codes (u - z') in fp16 (exact integers),
+//       B = query columns; for per-channel keys the per-channel scale is
+//           folded into the query (q * s_c), split into an fp16 hi and lo
+//           part placed in columns h and g + h, so the product keeps ~22 bits.
+//   O[row, c] = sum_t P[row, t] * V[t, c]
+//       P = p_t * s_t (value scale folded into the softmax weight), again as
+//           hi/lo rows h and g + h; V = value codes (u - z') in fp16.
+// Codes become fp16 by OR-ing them into the mantissa of a power of two
+// ("magic" exponent) and subtracting that power plus the zero-point in one
+// packed fp16 operation. For values the magic exponent also absorbs the
+// wavefront's largest value-scale exponent, which keeps p * s within fp16.
+//
+// Work split: grid (split, KV head, sequence), 4 wavefronts per workgroup,
+// each wavefront owns every 4th 32-token tile of the split and keeps its own
+// online softmax; the wavefronts merge through LDS, and the splits of one
+// (sequence, KV head) merge in the workgroup that finishes last (a counter
+// per pair in the workspace, reset to zero by that workgroup).
 #include "kvq_device.h"
 
 namespace kvq {
 
 namespace {
 
-__device__ __forceinline__ void wave_sync_lds() {
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kMagic1024 = 0x64006400u;  // fp16 pair (1024, 1024)
+
+struct Frag {  // 8 fp16 MFMA operand values as 4 packed pairs
+  uint32_t p[4];
+};
+
+__device__ __forceinline__ h2v as_h2(uint32_t x) { return __builtin_bit_cast(h2v, x); }
+__device__ __forceinline__ uint32_t as_u32(h2v x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ uint32_t hsub2(uint32_t a, uint32_t b) {
+  return as_u32(as_h2(a) - as_h2(b));
+}
+
+__device__ __forceinline__ f4v mfma(const Frag& a, const Frag& b, f4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8v, a),
+                                                 __builtin_bit_cast(h8v, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 }
 
+// fp16 pair (RTZ) of two floats.
+__device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+// a with the 13 low mantissa bits cleared: the fp16-RTZ value of a (normal range).
+__device__ __forceinline__ float trunc16(float a) {
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) & 0xFFFFE000u);
+}
+
+// 8 codes of BITS bits -> 4 fp16 pairs (magic|code) - sub[p].
+// BITS 4: lo holds 8 nibbles; pair p = (nibble p, nibble p+4).
+// BITS 2: lo holds 8 two-bit fields in its byte lane `half`*2, *2+1; pair p =
+//         (field p, field p+4).
+// BITS 8: lo, hi hold 8 bytes; pair p = (byte 2p, byte 2p+1).
+// magic_b: for BITS 8, the magic's high byte replicated in all four bytes.
+template <int BITS>
+__device__ __forceinline__ Frag unpack8(uint32_t lo, uint32_t hi, int half, uint32_t magic,
+                                        uint32_t magic_b, const uint32_t* sub) {
+  Frag f;
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) f.p[p] = hsub2(((lo >> (4 * p)) & 0x000F000Fu) | magic, sub[p]);
+  } else if constexpr (BITS == 2) {
+    const uint32_t sp = half ? perm(0u, lo, 0x0C030C02u) : perm(0u, lo, 0x0C010C00u);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) f.p[p] = hsub2(((sp >> (2 * p)) & 0x00030003u) | magic, sub[p]);
+  } else {
+    f.p[0] = hsub2(perm(magic_b, lo, 0x04010400u), sub[0]);
+    f.p[1] = hsub2(perm(magic_b, lo, 0x04030402u), sub[1]);
+    f.p[2] = hsub2(perm(magic_b, hi, 0x04010400u), sub[2]);
+    f.p[3] = hsub2(perm(magic_b, hi, 0x04030402u), sub[3]);
+  }
+  return f;
+}
+
+// Per-lane registers of one 32-token tile (quantized keys).
+template <int KB, int VB, int KAXIS, bool SPARSE>
+struct Tile {
+  uint32_t k[2][KB];       // key codes of the two 16-token MFMA row blocks
+  uint32_t v[8][VB == 8 ? 2 : 1];  // value codes per 16-channel chunk
+  uint32_t vm[8];          // value meta of this lane's 8 output tokens
+  uint32_t km[KAXIS ? 2 : 10];  // channel axis: meta of the lane's 2 build channels;
+                                // token axis: 8 output-token metas + 2 A-row metas
+  uint32_t sp[SPARSE ? 16 : 1];
+};
+
 template <int KB, int VB, int KAXIS, int G, bool SPARSE>
-__global__ __launch_bounds__(256) void attn_valu_kernel(CacheView c, AttnPlan p, const uint16_t* q,
-                                                        float* ws) {
+struct Attn {
+  using T = Tile<KB, VB, KAXIS, SPARSE>;
+  static constexpr int kQMinK = -(1 << (KB - 1));
+  static constexpr int kQMinV = -(1 << (VB - 1));
+  static constexpr bool kPermK = KB != 8;  // k-slot pairs (i, i+4) for 4/2-bit keys
+  static constexpr bool kPermV = VB != 8;
+
+  // Lane's position in the MFMA layouts.
+  int lane, c16, grp;
+  const CacheView& c;
+  size_t bh;
+  int Q;  // quantized key tokens of the sequence
+
+  __device__ Attn(const CacheView& cv, size_t bh_, int Q_) : c(cv), bh(bh_), Q(Q_) {
+    lane = threadIdx.x & 63;
+    c16 = lane & 15;
+    grp = lane >> 4;
+  }
+
+  // Token (0..31 within the tile) of A row m in MFMA row block e.
+  __device__ static int a_token(int e, int m) { return 8 * (m >> 2) + 4 * e + (m & 3); }
+
+  __device__ void load(T& t, int t0) const {
+    // key codes: rows a_token(e, c16), bytes [grp*4*KB, +4*KB) of the row
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint8_t* row = c.k_codes + (bh * c.T + t0 + a_token(e, c16)) * (size_t)(16 * KB) + grp * 4 * KB;
+      if constexpr (KB == 4) {
+        const uint4 x = *reinterpret_cast<const uint4*>(row);
+        t.k[e][0] = x.x; t.k[e][1] = x.y; t.k[e][2] = x.z; t.k[e][3] = x.w;
+      } else if constexpr (KB == 8) {
+        const uint4 x = reinterpret_cast<const uint4*>(row)[0];
+        const uint4 y = reinterpret_cast<const uint4*>(row)[1];
+        t.k[e][0] = x.x; t.k[e][1] = x.y; t.k[e][2] = x.z; t.k[e][3] = x.w;
+        t.k[e][4] = y.x; t.k[e][5] = y.y; t.k[e][6] = y.z; t.k[e][7] = y.w;
+      } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(row);
+        t.k[e][0] = x.x; t.k[e][1] = x.y;
+      }
+    }
+    // value codes: channel 16j + c16, tokens 8grp .. 8grp+7 of the block
+    const uint8_t* vblk = c.v_codes + (bh * (c.T / kBlock) + t0 / kBlock) * (size_t)(kD * 4 * VB);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint8_t* rec = vblk + (16 * j + c16) * 4 * VB;
+      if constexpr (VB == 4) {
+        t.v[j][0] = reinterpret_cast<const uint32_t*>(rec)[grp];
+      } else if constexpr (VB == 8) {
+        const uint2 x = reinterpret_cast<const uint2*>(rec)[grp];
+        t.v[j][0] = x.x; t.v[j][1] = x.y;
+      } else {
+        t.v[j][0] = reinterpret_cast<const uint16_t*>(rec)[grp];
+      }
+    }
+    {
+      const uint4* vm = reinterpret_cast<const uint4*>(c.v_meta + bh * c.T + t0 + 8 * grp);
+      const uint4 a = vm[0], b = vm[1];
+      t.vm[0] = a.x; t.vm[1] = a.y; t.vm[2] = a.z; t.vm[3] = a.w;
+      t.vm[4] = b.x; t.vm[5] = b.y; t.vm[6] = b.z; t.vm[7] = b.w;
+    }
+    if constexpr (KAXIS) {
+      const uint32_t* mb = c.k_meta + (bh * (c.T / kBlock) + t0 / kBlock) * kD;
+      int c0, c1;
+      build_channels(c0, c1);
+      t.km[0] = mb[c0];
+      t.km[1] = mb[c1];
+    } else {
+      const uint4* km = reinterpret_cast<const uint4*>(c.k_meta + bh * c.T + t0 + 8 * grp);
+      const uint4 a = km[0], b = km[1];
+      t.km[0] = a.x; t.km[1] = a.y; t.km[2] = a.z; t.km[3] = a.w;
+      t.km[4] = b.x; t.km[5] = b.y; t.km[6] = b.z; t.km[7] = b.w;
+      t.km[8] = c.k_meta[bh * c.T + t0 + a_token(0, c16)];
+      t.km[9] = c.k_meta[bh * c.T + t0 + a_token(1, c16)];
+    }
+    if constexpr (SPARSE) {
+      const uint4* sp = reinterpret_cast<const uint4*>(c.k_sparse + (bh * c.T + t0 + 8 * grp) * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 x = sp[i];
+        t.sp[4 * i] = x.x; t.sp[4 * i + 1] = x.y; t.sp[4 * i + 2] = x.z; t.sp[4 * i + 3] = x.w;
+      }
+    }
+  }
+
+  // Channels whose scaled query this lane builds: slot pair p of octet q.
+  __device__ void build_channels(int& c0, int& c1) const {
+    const int q = lane >> 2, p = lane & 3;
+    if (kPermK) { c0 = 8 * q + p; c1 = c0 + 4; }
+    else { c0 = 8 * q + 2 * p; c1 = c0 + 1; }
+  }
+};
+
+// LDS per wavefront: the B operand of the key product for the current block
+// ([grp][column][chunk] fragments) and the per-channel subtrahends of the A
+// operand ([grp][chunk][pair]).
+struct WaveLds {
+  Frag qb[4][16][4];
+  uint32_t zc[4][4][4];
+};
+
+template <int G>
+struct MergeLds {
+  float o[4][2 * G][kD];
+  float m[4][G];
+  float l[4][G];
+};
+
+template <int KB, int VB, int KAXIS, int G, bool SPARSE>
+__global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, const uint16_t* __restrict__ q,
+                                                   float* __restrict__ out, float* __restrict__ ws) {
+  using A = Attn<KB, VB, KAXIS, G, SPARSE>;
+  using T = typename A::T;
+  static_assert(2 * G <= 16, "hi/lo query columns must fit 16");
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, w = tid >> 6;
   const int L = c.seq_len[b];
+  const int nsplit_b = (L + p.tokens_per_split - 1) / p.tokens_per_split;
+  if (split > 0 && split >= nsplit_b) return;  // beyond this sequence (split 0 always runs)
   const int Q = KAXIS ? L - L % c.R : L;
   const int ts0 = split * p.tokens_per_split;
   const int ts1 = min(ts0 + p.tokens_per_split, L);
   const size_t bh = (size_t)b * c.H + h;
+  A at(c, bh, Q);
+  const int lane = at.lane, c16 = at.c16, grp = at.grp;
 
-  __shared__ float qs[G][kD];
-  __shared__ float pw[4][G][32];
-  __shared__ uint32_t vm[4][32];
-  __shared__ float red_m[4][G], red_l[4][G];
-  __shared__ float red_o[4][G][kD];
+  union SharedU {
+    WaveLds wave[4];
+    MergeLds<G> merge;
+  };
+  __shared__ SharedU sh;
+  __shared__ float qsh[SPARSE ? G : 1][kD];
+  __shared__ int s_last;
 
-  for (int i = tid; i < G * kD; i += 256)
-    qs[i / kD][i % kD] = h2f(q[((size_t)b * p.Hq + h * G + i / kD) * kD + i % kD]) * p.scale;
-  __syncthreads();
+  // query heads of this KV head, pre-scaled by softmax_scale * log2(e)
+  const float qscale = p.scale * kLog2e;
+  const uint16_t* qg = q + ((size_t)b * p.Hq + (size_t)h * G) * kD;
+  if constexpr (SPARSE) {
+    for (int i = tid; i < G * kD; i += 256) qsh[i / kD][i % kD] = h2f(qg[i]) * qscale;
+    __syncthreads();
+  }
 
-  float m[G], l[G], o[G][2];
+  WaveLds& wl = sh.wave[w];
+  // build lanes: scaled query of 2 channels for every head (channel axis)
+  int bc0 = 0, bc1 = 0;
+  float qv0[G], qv1[G];
+  // B operand for token-axis keys: raw fp16 query columns (exact)
+  Frag qfrag[KAXIS ? 1 : 4];
+  if constexpr (KAXIS) {
+    at.build_channels(bc0, bc1);
 #pragma unroll
-  for (int i = 0; i < G; ++i) { m[i] = -INFINITY; l[i] = 0.f; o[i][0] = o[i][1] = 0.f; }
-
-  const int tau = lane & 31, half = lane >> 5;
-  for (int t0 = ts0 + w * kBlock; t0 < ts1; t0 += 4 * kBlock) {
-    const int nv = min(kBlock, ts1 - t0);
-    const int t = t0 + tau;
-    float dot[G];
+    for (int hh = 0; hh < G; ++hh) {
+      qv0[hh] = h2f(qg[hh * kD + bc0]) * qscale;
+      qv1[hh] = h2f(qg[hh * kD + bc1]) * qscale;
+    }
+    // columns >= 2G stay zero for the whole split
+    for (int i = lane; i < 4 * 16 * 4 * 4; i += 64) {
+      const int pp = i & 3, j = (i >> 2) & 3, n = (i >> 4) & 15, g4 = i >> 8;
+      if (n >= 2 * G) wl.qb[g4][n][j].p[pp] = 0u;
+    }
+  } else {
 #pragma unroll
-    for (int i = 0; i < G; ++i) dot[i] = 0.f;
-    if (tau < nv) {
-      if (t < Q) {
-        const uint8_t* row = c.k_codes + (bh * c.T + t) * (16 * KB);
-        const uint32_t mt = KAXIS ? 0u : c.k_meta[bh * c.T + t];
-        const uint32_t* mc = c.k_meta + (bh * (c.T / kBlock) + t / kBlock) * kD;
-        for (int cc = 0; cc < 64; ++cc) {
-          const int ch = half * 64 + cc;
-          const float kh = dequant(get_field(row, ch, KB), KAXIS ? mc[ch] : mt, KB);
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
-          for (int i = 0; i < G; ++i) dot[i] += qs[i][ch] * kh;
+      for (int pp = 0; pp < 4; ++pp) {
+        uint32_t v = 0;
+        if (c16 < G) {
+          const int base = 32 * grp + 8 * j;
+          const int ch0 = A::kPermK ? base + pp : base + 2 * pp;
+          const int ch1 = A::kPermK ? ch0 + 4 : ch0 + 1;
+          v = (uint32_t)qg[c16 * kD + ch0] | ((uint32_t)qg[c16 * kD + ch1] << 16);
         }
-        if (SPARSE && half == 0) {
-          const uint32_t sv = c.k_sparse[(bh * c.T + t) * 2];
-          const uint32_t sc = c.k_sparse[(bh * c.T + t) * 2 + 1];
-          const float v0 = h2f((uint16_t)(sv & 0xFFFFu)), v1 = h2f((uint16_t)(sv >> 16));
+        qfrag[j].p[pp] = v;
+      }
+    }
+  }
+
+  // This wavefront's tiles: k = first, first + 4, ... over [ts0, ts1).
+  const int ntiles = (ts1 - ts0 + kBlock - 1) / kBlock;
+  const int tq = (Q > ts0) ? min((Q - ts0 + kBlock - 1) / kBlock, ntiles) : 0;  // quantized tiles
+
+  // Largest value-scale exponent over this wavefront's tiles: the magic
+  // exponent of the value operand (keeps p * s <= 2 in fp16).
+  int vx;
+  {
+    float smax = 0.f;
+    for (int k = w + 4 * (lane >> 5); k < ntiles; k += 8) {
+      const int t = ts0 + k * kBlock + (lane & 31);
+      if (t < ts1) smax = fmaxf(smax, h2f((uint16_t)(c.v_meta[bh * c.T + t] & 0xFFFFu)));
+    }
 #pragma unroll
-          for (int i = 0; i < G; ++i) dot[i] += qs[i][sc & 0xFFFFu] * v0 + qs[i][sc >> 16] * v1;
+    for (int off = 32; off >= 1; off >>= 1) smax = fmaxf(smax, __shfl_xor(smax, off, 64));
+    int e = 0;
+    if (smax > 0.f) e = ((__builtin_bit_cast(uint32_t, smax) >> 23) & 0xFF) - 127;
+    vx = min(max(e, -24), 5);
+  }
+  const uint32_t vmagic1 = (uint32_t)(25 + vx) << 10;
+  const uint32_t vmagic = vmagic1 | (vmagic1 << 16);
+  const uint32_t vmagic_b = (vmagic1 >> 8) * 0x01010101u;
+  const float vpow = __builtin_ldexpf(1.0f, -vx);  // s * 2^-vx in [1, 2)
+  const h2v vpow2 = {(_Float16)__builtin_ldexpf(1.0f, vx), (_Float16)__builtin_ldexpf(1.0f, vx)};
+  const h2v vofs2 = {(_Float16)(1024 - A::kQMinV), (_Float16)(1024 - A::kQMinV)};
+
+  // row factors of the P operand: hi rows (c16 < G) keep p*s, lo rows take the
+  // residual p*s - rtz16(p*s), rows >= 2G are zero
+  const float rowkeep = (c16 < 2 * G) ? 1.f : 0.f;
+  const float rowlo = (c16 >= G && c16 < 2 * G) ? 1.f : 0.f;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f4v acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
+
+  // ---- one tile: scores -> online softmax -> P.V -------------------------
+  auto softmax_pv = [&](float (&sc)[8], const T& t, int t0) {
+    // sc[4e + r] is the score of token 8grp + 4e + r (log2 units)
+    const int nvalid = ts1 - t0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (8 * grp + 4 * (i >> 2) + (i & 3) >= nvalid) sc[i] = -INFINITY;
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run && c16 < 2 * G)) {
+      float ar[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, (4 * grp + r) & (G - 1), 64);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] *= ar[r];
+    }
+    m_run = m_new;
+    float pr[8];
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+      ls += pr[i];
+    }
+    l_run = l_run * alpha + ls;
+    // P operand: k-slot order of the value codes
+    Frag pf;
+    uint32_t vsub[4];
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sv = h2f((uint16_t)(t.vm[i] & 0xFFFFu)) * vpow * rowkeep;
+      const float x = pr[i] * sv;
+      pv[i] = x - rowlo * trunc16(x);
+    }
+    // value subtrahends (1024 + z') * 2^vx per token pair
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const int i0 = A::kPermV ? pp : 2 * pp;          // output-token index of the pair
+      const int i1 = A::kPermV ? pp + 4 : 2 * pp + 1;
+      // t.vm index: token 8grp + 4e + r is index 4e + r
+      pf.p[pp] = pk_rtz(pv[i0], pv[i1]);
+      const uint32_t zz = perm(t.vm[i1], t.vm[i0], 0x07060302u);  // (z_i0, z_i1)
+      vsub[pp] = as_u32((as_h2(zz) + vofs2) * vpow2);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const Frag vf = unpack8<VB>(t.v[j][0], VB == 8 ? t.v[j][VB == 8 ? 1 : 0] : 0u, 0, vmagic,
+                                  vmagic_b, vsub);
+      acc[j] = mfma(pf, vf, acc[j]);
+    }
+  };
+
+  // ---- quantized tiles ------------------------------------------------------
+  auto qk_quant = [&](const T& t, int t0, float (&sc)[8]) {
+    f4v s[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
+    if constexpr (KAXIS) {
+      // build the B operand (scaled query, hi/lo) and the A subtrahends of this block
+      {
+        const float s0 = h2f((uint16_t)(t.km[0] & 0xFFFFu)), s1 = h2f((uint16_t)(t.km[1] & 0xFFFFu));
+        const int bq = lane >> 2, bp = lane & 3, bg = bq >> 2, bj = bq & 3;
+        wave_lds_fence();
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float v0 = qv0[hh] * s0, v1 = qv1[hh] * s1;
+          wl.qb[bg][hh][bj].p[bp] = pk_rtz(v0, v1);
+          wl.qb[bg][G + hh][bj].p[bp] = pk_rtz(v0 - trunc16(v0), v1 - trunc16(v1));
         }
-      } else {
-        const uint16_t* rr = c.k_resid + (bh * c.R + (t - Q)) * kD;
-        for (int cc = 0; cc < 64; ++cc) {
-          const int ch = half * 64 + cc;
-          const float kh = h2f(rr[ch]);
+        const uint32_t zz = perm(t.km[1], t.km[0], 0x07060302u);
+        const h2v kofs = {(_Float16)(1024 - A::kQMinK), (_Float16)(1024 - A::kQMinK)};
+        wl.zc[bg][bj][bp] = as_u32(as_h2(zz) + kofs);
+        wave_lds_fence();
+      }
+      Frag qf[4];
+      uint32_t zsub[4][4];
 #pragma unroll
-          for (int i = 0; i < G; ++i) dot[i] += qs[i][ch] * kh;
+      for (int j = 0; j < 4; ++j) {
+        qf[j] = wl.qb[grp][c16][j];
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) zsub[j][pp] = wl.zc[grp][j][pp];
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          Frag kf;
+          if constexpr (KB == 4) kf = unpack8<4>(t.k[e][j], 0u, 0, kMagic1024, 0u, zsub[j]);
+          else if constexpr (KB == 8) kf = unpack8<8>(t.k[e][2 * j], t.k[e][2 * j + 1], 0, kMagic1024, 0x64646464u, zsub[j]);
+          else kf = unpack8<2>(t.k[e][j >> 1], 0u, j & 1, kMagic1024, 0u, zsub[j]);
+          s[e] = mfma(kf, qf[j], s[e]);
+        }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t zt = (t.km[8 + e] >> 16) | (t.km[8 + e] & 0xFFFF0000u);  // (z, z)
+        const h2v kofs = {(_Float16)(1024 - A::kQMinK), (_Float16)(1024 - A::kQMinK)};
+        const uint32_t zs = as_u32(as_h2(zt) + kofs);
+        const uint32_t zsub[4] = {zs, zs, zs, zs};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          Frag kf;
+          if constexpr (KB == 4) kf = unpack8<4>(t.k[e][j], 0u, 0, kMagic1024, 0u, zsub);
+          else if constexpr (KB == 8) kf = unpack8<8>(t.k[e][2 * j], t.k[e][2 * j + 1], 0, kMagic1024, 0x64646464u, zsub);
+          else kf = unpack8<2>(t.k[e][j >> 1], 0u, j & 1, kMagic1024, 0u, zsub);
+          s[e] = mfma(kf, qfrag[j], s[e]);
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < G; ++i) dot[i] += __shfl_xor(dot[i], 32, 64);
-    if (half == 0 && tau < nv) vm[w][tau] = c.v_meta[bh * c.T + t];
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const float sc = (tau < nv) ? dot[i] : -INFINITY;
-      float mt = sc;
-      for (int off = 16; off >= 1; off >>= 1) mt = fmaxf(mt, __shfl_xor(mt, off, 64));
-      const float mn = fmaxf(m[i], mt);
-      const float alpha = __expf(m[i] - mn);
-      const float pv = (tau < nv) ? __expf(sc - mn) : 0.f;
-      float ls = pv;
-      for (int off = 16; off >= 1; off >>= 1) ls += __shfl_xor(ls, off, 64);
-      l[i] = l[i] * alpha + ls;
-      m[i] = mn;
-      o[i][0] *= alpha;
-      o[i][1] *= alpha;
-      if (half == 0) pw[w][i][tau] = pv;
-    }
-    wave_sync_lds();
-    const uint8_t* vblk = c.v_codes + (bh * (c.T / kBlock) + t0 / kBlock) * (size_t)(kD * 4 * VB);
+      for (int r = 0; r < 4; ++r) {
+        float v = s[e][r];
+        v += __shfl_xor(v, G, 64);  // hi + lo columns (token-axis: adds the zero column)
+        if constexpr (!KAXIS) v *= h2f((uint16_t)(t.km[4 * e + r] & 0xFFFFu)) * qscale;
+        sc[4 * e + r] = v;
+      }
+    if constexpr (SPARSE) {
+      const int hq = c16 & (G - 1);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int ch = 2 * lane + k;
-      const uint8_t* rec = vblk + ch * 4 * VB;
-      for (int tt = 0; tt < nv; ++tt) {
-        const float vh = dequant(get_field(rec, tt, VB), vm[w][tt], VB);
-#pragma unroll
-        for (int i = 0; i < G; ++i) o[i][k] += pw[w][i][tt] * vh;
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t sv = t.sp[2 * i], scol = t.sp[2 * i + 1];
+        sc[i] += qsh[hq][scol & 0xFFFFu] * h2f((uint16_t)(sv & 0xFFFFu)) +
+                 qsh[hq][scol >> 16] * h2f((uint16_t)(sv >> 16));
       }
     }
-    wave_sync_lds();
+  };
+
+  int k = w;
+  if (k < tq) {
+    T ta, tb;
+    at.load(ta, ts0 + k * kBlock);
+    while (true) {
+      float sc[8];
+      if (k + 4 < tq) at.load(tb, ts0 + (k + 4) * kBlock);
+      qk_quant(ta, ts0 + k * kBlock, sc);
+      softmax_pv(sc, ta, ts0 + k * kBlock);
+      k += 4;
+      if (k >= tq) break;
+      if (k + 4 < tq) at.load(ta, ts0 + (k + 4) * kBlock);
+      qk_quant(tb, ts0 + k * kBlock, sc);
+      softmax_pv(sc, tb, ts0 + k * kBlock);
+      k += 4;
+      if (k >= tq) break;
+    }
+  }
+  // ---- residual (fp16) key tiles: channel axis only ------------------------
+  if constexpr (KAXIS) {
+    for (k = (tq + ((w - tq) % 4 + 4) % 4); k < ntiles; k += 4) {
+      const int t0 = ts0 + k * kBlock;
+      T t;
+      // value side of the tile
+      {
+        const uint8_t* vblk = c.v_codes + (bh * (c.T / kBlock) + t0 / kBlock) * (size_t)(kD * 4 * VB);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint8_t* rec = vblk + (16 * j + c16) * 4 * VB;
+          if constexpr (VB == 4) t.v[j][0] = reinterpret_cast<const uint32_t*>(rec)[grp];
+          else if constexpr (VB == 8) {
+            const uint2 x = reinterpret_cast<const uint2*>(rec)[grp];
+            t.v[j][0] = x.x; t.v[j][VB == 8 ? 1 : 0] = x.y;
+          } else t.v[j][0] = reinterpret_cast<const uint16_t*>(rec)[grp];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int tt = t0 + 8 * grp + i;
+          t.vm[i] = (tt < ts1) ? c.v_meta[bh * c.T + tt] : 0u;
+        }
+      }
+      // B operand: unscaled-by-meta query (s = 1), hi/lo
+      {
+        const int bq = lane >> 2, bp = lane & 3, bg = bq >> 2, bj = bq & 3;
+        wave_lds_fence();
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float v0 = qv0[hh], v1 = qv1[hh];
+          wl.qb[bg][hh][bj].p[bp] = pk_rtz(v0, v1);
+          wl.qb[bg][G + hh][bj].p[bp] = pk_rtz(v0 - trunc16(v0), v1 - trunc16(v1));
+        }
+        wave_lds_fence();
+      }
+      f4v s[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int tt = t0 + A::a_token(e, c16);
+        const bool ok = tt < ts1;
+        const uint16_t* kr = c.k_resid + (bh * c.R + (ok ? tt - Q : 0)) * kD + 32 * grp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint4 x = ok ? reinterpret_cast<const uint4*>(kr + 8 * j)[0] : make_uint4(0, 0, 0, 0);
+          Frag kf;
+          if (A::kPermK) {  // pairs (channel p, p+4)
+            kf.p[0] = perm(x.z, x.x, 0x05040100u);
+            kf.p[1] = perm(x.z, x.x, 0x07060302u);
+            kf.p[2] = perm(x.w, x.y, 0x05040100u);
+            kf.p[3] = perm(x.w, x.y, 0x07060302u);
+          } else {
+            kf.p[0] = x.x; kf.p[1] = x.y; kf.p[2] = x.z; kf.p[3] = x.w;
+          }
+          s[e] = mfma(kf, wl.qb[grp][c16][j], s[e]);
+        }
+      }
+      float sc[8];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = s[e][r];
+          v += __shfl_xor(v, G, 64);
+          sc[4 * e + r] = v;
+        }
+      softmax_pv(sc, t, t0);
+    }
   }
 
+  // ---- merge the wavefronts of the workgroup --------------------------------
+  {
+    float lsum = l_run;
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    __syncthreads();  // every wavefront is done with its WaveLds
+    MergeLds<G>& mg = sh.merge;
+    if (grp == 0 && c16 < G) {
+      mg.m[w][c16] = m_run;
+      mg.l[w][c16] = lsum;
+    }
 #pragma unroll
-  for (int i = 0; i < G; ++i) {
-    red_o[w][i][2 * lane] = o[i][0];
-    red_o[w][i][2 * lane + 1] = o[i][1];
-    if (lane == 0) { red_m[w][i] = m[i]; red_l[w][i] = l[i]; }
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * grp + r;
+        if (row < 2 * G) mg.o[w][row][16 * j + c16] = acc[j][r];
+      }
   }
   __syncthreads();
+  MergeLds<G>& mg = sh.merge;
+  const bool single = nsplit_b <= 1;
+  float* part_base = ws + kPartialOffsetFloats(c.B, c.H);
   for (int e = tid; e < G * kD; e += 256) {
-    const int i = e / kD, ch = e % kD;
-    float M = red_m[0][i];
-    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, red_m[ww][i]);
-    float acc = 0.f, lsum = 0.f;
+    const int hh = e / kD, ch = e % kD;
+    float M = mg.m[0][hh];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, mg.m[ww][hh]);
+    float o = 0.f, l = 0.f;
     if (M != -INFINITY) {
+#pragma unroll
       for (int ww = 0; ww < 4; ++ww) {
-        const float f = __expf(red_m[ww][i] - M);
-        acc += f * red_o[ww][i][ch];
-        lsum += f * red_l[ww][i];
+        const float f = __builtin_amdgcn_exp2f(mg.m[ww][hh] - M);
+        o += f * (mg.o[ww][hh][ch] + mg.o[ww][G + hh][ch]);
+        l += f * mg.l[ww][hh];
       }
     }
-    float* part = ws + (((size_t)b * p.Hq + h * G + i) * p.n_split + split) * kPartialFloats;
-    if (ch == 0) { part[0] = M; part[1] = lsum; part[2] = 0.f; part[3] = 0.f; }
-    part[4 + ch] = acc;
-  }
-}
-
-// Log-sum-exp merge of the split partials: one workgroup per (sequence,
-// query head), one thread per channel.
-__global__ __launch_bounds__(128) void combine_kernel(const float* ws, float* out, int n_split) {
-  const int bq = blockIdx.x, ch = threadIdx.x;
-  const float* part = ws + (size_t)bq * n_split * kPartialFloats;
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part[s * kPartialFloats]);
-  float acc = 0.f, lsum = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n_split; ++s) {
-      const float f = __expf(part[s * kPartialFloats] - M);
-      acc += f * part[s * kPartialFloats + 4 + ch];
-      lsum += f * part[s * kPartialFloats + 1];
+    const size_t qh = (size_t)b * p.Hq + (size_t)h * G + hh;
+    if (single) {
+      out[qh * kD + ch] = (l > 0.f) ? o / l : 0.f;
+    } else {
+      float* part = part_base + (qh * p.n_split + split) * kPartialFloats;
+      if (ch == 0) { part[0] = M; part[1] = l; }
+      part[4 + ch] = o;
     }
   }
-  out[(size_t)bq * kD + ch] = (lsum > 0.f) ? acc / lsum : 0.f;
+  if (single) return;
+
+  // ---- the last workgroup of this (sequence, KV head) merges the splits -----
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    int* ctr = reinterpret_cast<int*>(ws) + bh;
+    const int prev = atomicAdd(ctr, 1);
+    s_last = (prev == nsplit_b - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int e = tid; e < G * kD; e += 256) {
+    const int hh = e / kD, ch = e % kD;
+    const size_t qh = (size_t)b * p.Hq + (size_t)h * G + hh;
+    const float* part = part_base + qh * p.n_split * kPartialFloats;
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < nsplit_b; ++s2) M = fmaxf(M, part[s2 * kPartialFloats]);
+    float o = 0.f, l = 0.f;
+    if (M != -INFINITY) {
+      for (int s2 = 0; s2 < nsplit_b; ++s2) {
+        const float f = __builtin_amdgcn_exp2f(part[s2 * kPartialFloats] - M);
+        o += f * part[s2 * kPartialFloats + 4 + ch];
+        l += f * part[s2 * kPartialFloats + 1];
+      }
+    }
+    out[qh * kD + ch] = (l > 0.f) ? o / l : 0.f;
+  }
+  if (tid == 0) reinterpret_cast<int*>(ws)[bh] = 0;
 }
 
 template <int KB, int VB, int KAXIS, int G, bool SPARSE>
-hipError_t launch_t(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* ws,
+hipError_t launch_t(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
                     hipStream_t st) {
   dim3 grid(p.n_split, c.H, c.B);
-  hipLaunchKernelGGL((attn_valu_kernel<KB, VB, KAXIS, G, SPARSE>), grid, dim3(256), 0, st, c, p, q,
-                     ws);
+  hipLaunchKernelGGL((attn_kernel<KB, VB, KAXIS, G, SPARSE>), grid, dim3(256), 0, st, c, p, q, out, ws);
   return hipGetLastError();
 }
 
 template <int KB, int VB, int KAXIS, bool SPARSE>
-hipError_t dispatch_g(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* ws,
+hipError_t dispatch_g(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
                       hipStream_t st) {
   switch (p.group) {
-    case 1: return launch_t<KB, VB, KAXIS, 1, SPARSE>(c, p, q, ws, st);
-    case 2: return launch_t<KB, VB, KAXIS, 2, SPARSE>(c, p, q, ws, st);
-    case 4: return launch_t<KB, VB, KAXIS, 4, SPARSE>(c, p, q, ws, st);
-    case 8: return launch_t<KB, VB, KAXIS, 8, SPARSE>(c, p, q, ws, st);
+    case 1: return launch_t<KB, VB, KAXIS, 1, SPARSE>(c, p, q, out, ws, st);
+    case 2: return launch_t<KB, VB, KAXIS, 2, SPARSE>(c, p, q, out, ws, st);
+    case 4: return launch_t<KB, VB, KAXIS, 4, SPARSE>(c, p, q, out, ws, st);
+    case 8: return launch_t<KB, VB, KAXIS, 8, SPARSE>(c, p, q, out, ws, st);
   }
   return hipErrorInvalidValue;
 }
 
 template <int KB, int VB>
-hipError_t dispatch_axis(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* ws,
+hipError_t dispatch_axis(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
                          hipStream_t st) {
-  if (c.kaxis == 0) return dispatch_g<KB, VB, 0, false>(c, p, q, ws, st);
-  if (c.sparse) return dispatch_g<KB, VB, 1, true>(c, p, q, ws, st);
-  return dispatch_g<KB, VB, 1, false>(c, p, q, ws, st);
+  if (c.kaxis == 0) return dispatch_g<KB, VB, 0, false>(c, p, q, out, ws, st);
+  if (c.sparse) return dispatch_g<KB, VB, 1, true>(c, p, q, out, ws, st);
+  return dispatch_g<KB, VB, 1, false>(c, p, q, out, ws, st);
 }
 
 template <int KB>
-hipError_t dispatch_vb(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* ws,
+hipError_t dispatch_vb(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
                        hipStream_t st) {
   switch (c.vbits) {
-    case 8: return dispatch_axis<KB, 8>(c, p, q, ws, st);
-    case 4: return dispatch_axis<KB, 4>(c, p, q, ws, st);
-    case 2: return dispatch_axis<KB, 2>(c, p, q, ws, st);
+    case 8: return dispatch_axis<KB, 8>(c, p, q, out, ws, st);
+    case 4: return dispatch_axis<KB, 4>(c, p, q, out, ws, st);
+    case 2: return dispatch_axis<KB, 2>(c, p, q, out, ws, st);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p, const uint16_t* q,
-                                   float* out, float* ws, hipStream_t st) {
-  hipError_t e;
+hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out,
+                                   float* ws, hipStream_t st) {
   switch (c.kbits) {
-    case 8: e = dispatch_vb<8>(c, p, q, ws, st); break;
-    case 4: e = dispatch_vb<4>(c, p, q, ws, st); break;
-    case 2: e = dispatch_vb<2>(c, p, q, ws, st); break;
-    default: return hipErrorInvalidValue;
+    case 8: return dispatch_vb<8>(c, p, q, out, ws, st);
+    case 4: return dispatch_vb<4>(c, p, q, out, ws, st);
+    case 2: return dispatch_vb<2>(c, p, q, out, ws, st);
   }
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(c.B * p.Hq), dim3(kD), 0, st, ws, out, p.n_split);
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvq
