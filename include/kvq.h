@@ -195,10 +195,9 @@ kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache,
  * where K_hat / V_hat are the dequantized codes (plus sparse entries), and
  * residual keys are the stored fp16 values. A sequence with no tokens gets
  * out = 0. ws is device workspace of at least kvq_workspace_bytes(cfg,
- * cache->batch, cache->max_tokens) bytes. It holds one split counter per
- * (sequence, KV head) followed by split partial results; it must be
- * zero-filled before its first use, and every call leaves the counters at
- * zero again. Calls that share a workspace must be ordered on one stream.
+ * cache->batch, cache->max_tokens) bytes for split partial results; its
+ * contents need no initial value. Calls that share a workspace must be
+ * ordered on one stream.
  * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EWORKSPACE, KVQ_EHIP. */
 kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 const void* q, float* out, float softmax_scale,

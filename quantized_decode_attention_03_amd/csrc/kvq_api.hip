@@ -6,7 +6,7 @@
 
 #include <algorithm>
 
-#include "../../include/kvq.h"
+#include "kvq.h"
 #include "kvq_internal.h"
 
 using namespace kvq;
@@ -140,9 +140,7 @@ kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch, int32_t max_tok
 
 size_t kvq_workspace_bytes(const kvq_config* cfg, int32_t batch, int32_t max_tokens) {
   if (check_config(cfg) != KVQ_OK || check_shape(batch, max_tokens) != KVQ_OK) return 0;
-  return (kPartialOffsetFloats(batch, cfg->n_kv_heads) +
-          (size_t)batch * cfg->n_q_heads * max_splits_for(max_tokens) * kPartialFloats) *
-         sizeof(float);
+  return (size_t)batch * cfg->n_q_heads * max_splits_for(max_tokens) * kPartialFloats * sizeof(float);
 }
 
 kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new, const void* v_new,

@@ -26,9 +26,11 @@
 //
 // Work split: grid (split, KV head, sequence), 4 wavefronts per workgroup,
 // each wavefront owns every 4th 32-token tile of the split and keeps its own
-// online softmax; the wavefronts merge through LDS, and the splits of one
-// (sequence, KV head) merge in the workgroup that finishes last (a counter
-// per pair in the workspace, reset to zero by that workgroup).
+// online softmax; the wavefronts merge through LDS. Sequences longer than one
+// split leave (m, l, o) partials in the workspace that a second, small kernel
+// merges with a log-sum-exp. (Merging in the last-arriving workgroup instead
+// needs device-scope fences, whose L2 writeback and invalidation cost far more
+// than the extra launch on this chip.)
 #include "kvq_device.h"
 
 namespace kvq {
@@ -206,10 +208,11 @@ struct Attn {
 };
 
 // LDS per wavefront: the B operand of the key product for the current block
-// ([grp][column][chunk] fragments) and the per-channel subtrahends of the A
-// operand ([grp][chunk][pair]).
+// (hi rows 0..G-1, lo rows G..2G-1, an all-zero row 2G; [grp][row][chunk]
+// fragments) and the per-channel subtrahends of the A operand
+// ([grp][chunk][pair]).
 struct WaveLds {
-  Frag qb[4][16][4];
+  Frag qb[4][17][4];
   uint32_t zc[4][4][4];
 };
 
@@ -220,14 +223,31 @@ struct MergeLds {
   float l[4][G];
 };
 
+// max / sum over lanes l, l^16, l^32, l^48 (the four lane groups of one
+// column); used only when the softmax reference moves and once per split
+__device__ __forceinline__ float grp_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float grp_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+
+// The softmax reference m of a head moves only when a score exceeds it by
+// more than 2^kLazy (log2 units), so most tiles need no cross-lane maximum and
+// no rescaling; weights stay <= 2^kLazy.
+constexpr float kLazy = 8.f;
+
 template <int KB, int VB, int KAXIS, int G, bool SPARSE>
 __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, const uint16_t* __restrict__ q,
                                                    float* __restrict__ out, float* __restrict__ ws) {
   using A = Attn<KB, VB, KAXIS, G, SPARSE>;
   using T = typename A::T;
-  static_assert(2 * G <= 16, "hi/lo query columns must fit 16");
+  static_assert(2 * G <= 16, "hi/lo rows must fit 16");
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int L = c.seq_len[b];
   const int nsplit_b = (L + p.tokens_per_split - 1) / p.tokens_per_split;
   if (split > 0 && split >= nsplit_b) return;  // beyond this sequence (split 0 always runs)
@@ -237,6 +257,8 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   const size_t bh = (size_t)b * c.H + h;
   A at(c, bh, Q);
   const int lane = at.lane, c16 = at.c16, grp = at.grp;
+  const int hq = c16 & (G - 1);           // head of this lane's column / row
+  const bool live = c16 < 2 * G;          // lanes whose column / row is used
 
   union SharedU {
     WaveLds wave[4];
@@ -244,7 +266,6 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   };
   __shared__ SharedU sh;
   __shared__ float qsh[SPARSE ? G : 1][kD];
-  __shared__ int s_last;
 
   // query heads of this KV head, pre-scaled by softmax_scale * log2(e)
   const float qscale = p.scale * kLog2e;
@@ -255,11 +276,14 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   }
 
   WaveLds& wl = sh.wave[w];
-  // build lanes: scaled query of 2 channels for every head (channel axis)
+  // channel axis: this lane builds the scaled query of 2 channels, all heads
   int bc0 = 0, bc1 = 0;
   float qv0[G], qv1[G];
-  // B operand for token-axis keys: raw fp16 query columns (exact)
+  // token axis: the B operand is the raw fp16 query (exact), column n = head n mod G
   Frag qfrag[KAXIS ? 1 : 4];
+  // rows of the key-product B operand this lane reads (the zero row when unused)
+  const int brow_hi = live ? hq : 2 * G;
+  const int brow_lo = live ? G + hq : 2 * G;
   if constexpr (KAXIS) {
     at.build_channels(bc0, bc1);
 #pragma unroll
@@ -267,34 +291,30 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
       qv0[hh] = h2f(qg[hh * kD + bc0]) * qscale;
       qv1[hh] = h2f(qg[hh * kD + bc1]) * qscale;
     }
-    // columns >= 2G stay zero for the whole split
-    for (int i = lane; i < 4 * 16 * 4 * 4; i += 64) {
-      const int pp = i & 3, j = (i >> 2) & 3, n = (i >> 4) & 15, g4 = i >> 8;
-      if (n >= 2 * G) wl.qb[g4][n][j].p[pp] = 0u;
-    }
+    if (lane < 16) wl.qb[lane >> 2][2 * G][lane & 3] = Frag{{0u, 0u, 0u, 0u}};
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
         uint32_t v = 0;
-        if (c16 < G) {
+        if (live) {
           const int base = 32 * grp + 8 * j;
           const int ch0 = A::kPermK ? base + pp : base + 2 * pp;
           const int ch1 = A::kPermK ? ch0 + 4 : ch0 + 1;
-          v = (uint32_t)qg[c16 * kD + ch0] | ((uint32_t)qg[c16 * kD + ch1] << 16);
+          v = (uint32_t)qg[hq * kD + ch0] | ((uint32_t)qg[hq * kD + ch1] << 16);
         }
         qfrag[j].p[pp] = v;
       }
     }
   }
 
-  // This wavefront's tiles: k = first, first + 4, ... over [ts0, ts1).
+  // This wavefront's tiles: k = w, w + 4, ... over [ts0, ts1).
   const int ntiles = (ts1 - ts0 + kBlock - 1) / kBlock;
   const int tq = (Q > ts0) ? min((Q - ts0 + kBlock - 1) / kBlock, ntiles) : 0;  // quantized tiles
 
   // Largest value-scale exponent over this wavefront's tiles: the magic
-  // exponent of the value operand (keeps p * s <= 2 in fp16).
+  // exponent of the value operand (keeps p * s small in fp16).
   int vx;
   {
     float smax = 0.f;
@@ -302,25 +322,28 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
       const int t = ts0 + k * kBlock + (lane & 31);
       if (t < ts1) smax = fmaxf(smax, h2f((uint16_t)(c.v_meta[bh * c.T + t] & 0xFFFFu)));
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) smax = fmaxf(smax, __shfl_xor(smax, off, 64));
+    smax = fmaxf(smax, __shfl_xor(smax, 1, 64));
+    smax = fmaxf(smax, __shfl_xor(smax, 2, 64));
+    smax = fmaxf(smax, __shfl_xor(smax, 4, 64));
+    smax = fmaxf(smax, __shfl_xor(smax, 8, 64));
+    smax = grp_max(smax);
     int e = 0;
     if (smax > 0.f) e = ((__builtin_bit_cast(uint32_t, smax) >> 23) & 0xFF) - 127;
-    vx = min(max(e, -24), 5);
+    vx = __builtin_amdgcn_readfirstlane(min(max(e, -24), 5));
   }
   const uint32_t vmagic1 = (uint32_t)(25 + vx) << 10;
   const uint32_t vmagic = vmagic1 | (vmagic1 << 16);
   const uint32_t vmagic_b = (vmagic1 >> 8) * 0x01010101u;
-  const float vpow = __builtin_ldexpf(1.0f, -vx);  // s * 2^-vx in [1, 2)
+  const float vpow = __builtin_ldexpf(1.0f, -vx);  // s * 2^-vx < 2 for the largest s
   const h2v vpow2 = {(_Float16)__builtin_ldexpf(1.0f, vx), (_Float16)__builtin_ldexpf(1.0f, vx)};
   const h2v vofs2 = {(_Float16)(1024 - A::kQMinV), (_Float16)(1024 - A::kQMinV)};
 
   // row factors of the P operand: hi rows (c16 < G) keep p*s, lo rows take the
   // residual p*s - rtz16(p*s), rows >= 2G are zero
-  const float rowkeep = (c16 < 2 * G) ? 1.f : 0.f;
-  const float rowlo = (c16 >= G && c16 < 2 * G) ? 1.f : 0.f;
+  const float rowkeep = live ? vpow : 0.f;
+  const float rowlo = (c16 >= G && live) ? 1.f : 0.f;
 
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
   f4v acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
@@ -329,17 +352,15 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   auto softmax_pv = [&](float (&sc)[8], const T& t, int t0) {
     // sc[4e + r] is the score of token 8grp + 4e + r (log2 units)
     const int nvalid = ts1 - t0;
+    float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
       if (8 * grp + 4 * (i >> 2) + (i & 3) >= nvalid) sc[i] = -INFINITY;
-    float mx = sc[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run && c16 < 2 * G)) {
+      mx = fmaxf(mx, sc[i]);
+    }
+    if (__builtin_amdgcn_ballot_w64(live && mx > m_ref + kLazy)) {
+      const float m_new = fmaxf(m_ref, grp_max(mx));
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
       float ar[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, (4 * grp + r) & (G - 1), 64);
@@ -347,32 +368,28 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
       for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[j][r] *= ar[r];
+      l_run *= alpha;
+      m_ref = m_new;
     }
-    m_run = m_new;
     float pr[8];
-    float ls = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
-      ls += pr[i];
+      pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_ref);
+      l_run += pr[i];
     }
-    l_run = l_run * alpha + ls;
-    // P operand: k-slot order of the value codes
+    // P operand (k-slot order of the value codes) and value subtrahends
     Frag pf;
     uint32_t vsub[4];
     float pv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float sv = h2f((uint16_t)(t.vm[i] & 0xFFFFu)) * vpow * rowkeep;
-      const float x = pr[i] * sv;
+      const float x = pr[i] * (h2f((uint16_t)(t.vm[i] & 0xFFFFu)) * rowkeep);
       pv[i] = x - rowlo * trunc16(x);
     }
-    // value subtrahends (1024 + z') * 2^vx per token pair
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      const int i0 = A::kPermV ? pp : 2 * pp;          // output-token index of the pair
+      const int i0 = A::kPermV ? pp : 2 * pp;
       const int i1 = A::kPermV ? pp + 4 : 2 * pp + 1;
-      // t.vm index: token 8grp + 4e + r is index 4e + r
       pf.p[pp] = pk_rtz(pv[i0], pv[i1]);
       const uint32_t zz = perm(t.vm[i1], t.vm[i0], 0x07060302u);  // (z_i0, z_i1)
       vsub[pp] = as_u32((as_h2(zz) + vofs2) * vpow2);
@@ -385,11 +402,11 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     }
   };
 
-  // ---- quantized tiles ------------------------------------------------------
-  auto qk_quant = [&](const T& t, int t0, float (&sc)[8]) {
+  // key product of one tile; fills sc[8]
+  auto qk_quant = [&](const T& t, float (&sc)[8]) {
     f4v s[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
     if constexpr (KAXIS) {
-      // build the B operand (scaled query, hi/lo) and the A subtrahends of this block
+      // B operand (scaled query, hi/lo) and A subtrahends of this block
       {
         const float s0 = h2f((uint16_t)(t.km[0] & 0xFFFFu)), s1 = h2f((uint16_t)(t.km[1] & 0xFFFFu));
         const int bq = lane >> 2, bp = lane & 3, bg = bq >> 2, bj = bq & 3;
@@ -405,24 +422,27 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
         wl.zc[bg][bj][bp] = as_u32(as_h2(zz) + kofs);
         wave_lds_fence();
       }
-      Frag qf[4];
-      uint32_t zsub[4][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        qf[j] = wl.qb[grp][c16][j];
+        const Frag qh = wl.qb[grp][brow_hi][j];
+        const Frag ql = wl.qb[grp][brow_lo][j];
+        uint32_t zsub[4];
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) zsub[j][pp] = wl.zc[grp][j][pp];
+        for (int pp = 0; pp < 4; ++pp) zsub[pp] = wl.zc[grp][j][pp];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          Frag kf;
+          if constexpr (KB == 4) kf = unpack8<4>(t.k[e][j], 0u, 0, kMagic1024, 0u, zsub);
+          else if constexpr (KB == 8) kf = unpack8<8>(t.k[e][2 * j], t.k[e][2 * j + 1], 0, kMagic1024, 0x64646464u, zsub);
+          else kf = unpack8<2>(t.k[e][j >> 1], 0u, j & 1, kMagic1024, 0u, zsub);
+          s[e] = mfma(kf, qh, s[e]);
+          s[e] = mfma(kf, ql, s[e]);
+        }
       }
 #pragma unroll
       for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          Frag kf;
-          if constexpr (KB == 4) kf = unpack8<4>(t.k[e][j], 0u, 0, kMagic1024, 0u, zsub[j]);
-          else if constexpr (KB == 8) kf = unpack8<8>(t.k[e][2 * j], t.k[e][2 * j + 1], 0, kMagic1024, 0x64646464u, zsub[j]);
-          else kf = unpack8<2>(t.k[e][j >> 1], 0u, j & 1, kMagic1024, 0u, zsub[j]);
-          s[e] = mfma(kf, qf[j], s[e]);
-        }
+        for (int r = 0; r < 4; ++r) sc[4 * e + r] = s[e][r];
     } else {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -439,18 +459,13 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           s[e] = mfma(kf, qfrag[j], s[e]);
         }
       }
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sc[4 * e + r] = s[e][r] * (h2f((uint16_t)(t.km[4 * e + r] & 0xFFFFu)) * qscale);
     }
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = s[e][r];
-        v += __shfl_xor(v, G, 64);  // hi + lo columns (token-axis: adds the zero column)
-        if constexpr (!KAXIS) v *= h2f((uint16_t)(t.km[4 * e + r] & 0xFFFFu)) * qscale;
-        sc[4 * e + r] = v;
-      }
     if constexpr (SPARSE) {
-      const int hq = c16 & (G - 1);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t sv = t.sp[2 * i], scol = t.sp[2 * i + 1];
@@ -460,30 +475,31 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     }
   };
 
-  int k = w;
-  if (k < tq) {
+  // ---- quantized tiles, one tile of loads in flight ahead -------------------
+  if (w < tq) {
     T ta, tb;
+    const int klast = tq - 1 - ((tq - 1 - w) & 3);  // last tile of this wavefront
+    int k = w;
     at.load(ta, ts0 + k * kBlock);
     while (true) {
       float sc[8];
-      if (k + 4 < tq) at.load(tb, ts0 + (k + 4) * kBlock);
-      qk_quant(ta, ts0 + k * kBlock, sc);
+      at.load(tb, ts0 + min(k + 4, klast) * kBlock);
+      qk_quant(ta, sc);
       softmax_pv(sc, ta, ts0 + k * kBlock);
       k += 4;
-      if (k >= tq) break;
-      if (k + 4 < tq) at.load(ta, ts0 + (k + 4) * kBlock);
-      qk_quant(tb, ts0 + k * kBlock, sc);
+      if (k > klast) break;
+      at.load(ta, ts0 + min(k + 4, klast) * kBlock);
+      qk_quant(tb, sc);
       softmax_pv(sc, tb, ts0 + k * kBlock);
       k += 4;
-      if (k >= tq) break;
+      if (k > klast) break;
     }
   }
   // ---- residual (fp16) key tiles: channel axis only ------------------------
   if constexpr (KAXIS) {
-    for (k = (tq + ((w - tq) % 4 + 4) % 4); k < ntiles; k += 4) {
+    for (int k = tq + ((w - tq) % 4 + 4) % 4; k < ntiles; k += 4) {
       const int t0 = ts0 + k * kBlock;
       T t;
-      // value side of the tile
       {
         const uint8_t* vblk = c.v_codes + (bh * (c.T / kBlock) + t0 / kBlock) * (size_t)(kD * 4 * VB);
 #pragma unroll
@@ -495,13 +511,12 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
             t.v[j][0] = x.x; t.v[j][VB == 8 ? 1 : 0] = x.y;
           } else t.v[j][0] = reinterpret_cast<const uint16_t*>(rec)[grp];
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int tt = t0 + 8 * grp + i;
-          t.vm[i] = (tt < ts1) ? c.v_meta[bh * c.T + tt] : 0u;
-        }
+        const uint4* vm = reinterpret_cast<const uint4*>(c.v_meta + bh * c.T + t0 + 8 * grp);
+        const uint4 a = vm[0], bb = vm[1];
+        t.vm[0] = a.x; t.vm[1] = a.y; t.vm[2] = a.z; t.vm[3] = a.w;
+        t.vm[4] = bb.x; t.vm[5] = bb.y; t.vm[6] = bb.z; t.vm[7] = bb.w;
       }
-      // B operand: unscaled-by-meta query (s = 1), hi/lo
+      // B operand: query scaled by the softmax factor only, hi/lo
       {
         const int bq = lane >> 2, bp = lane & 3, bg = bq >> 2, bj = bq & 3;
         wave_lds_fence();
@@ -521,7 +536,8 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
         const uint16_t* kr = c.k_resid + (bh * c.R + (ok ? tt - Q : 0)) * kD + 32 * grp;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          uint4 x = ok ? reinterpret_cast<const uint4*>(kr + 8 * j)[0] : make_uint4(0, 0, 0, 0);
+          uint4 x = reinterpret_cast<const uint4*>(kr + 8 * j)[0];
+          if (!ok) x = make_uint4(0, 0, 0, 0);
           Frag kf;
           if (A::kPermK) {  // pairs (channel p, p+4)
             kf.p[0] = perm(x.z, x.x, 0x05040100u);
@@ -531,31 +547,26 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           } else {
             kf.p[0] = x.x; kf.p[1] = x.y; kf.p[2] = x.z; kf.p[3] = x.w;
           }
-          s[e] = mfma(kf, wl.qb[grp][c16][j], s[e]);
+          s[e] = mfma(kf, wl.qb[grp][brow_hi][j], s[e]);
+          s[e] = mfma(kf, wl.qb[grp][brow_lo][j], s[e]);
         }
       }
       float sc[8];
 #pragma unroll
       for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = s[e][r];
-          v += __shfl_xor(v, G, 64);
-          sc[4 * e + r] = v;
-        }
+        for (int r = 0; r < 4; ++r) sc[4 * e + r] = s[e][r];
       softmax_pv(sc, t, t0);
     }
   }
 
   // ---- merge the wavefronts of the workgroup --------------------------------
   {
-    float lsum = l_run;
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+    const float lsum = grp_sum(l_run);
     __syncthreads();  // every wavefront is done with its WaveLds
     MergeLds<G>& mg = sh.merge;
     if (grp == 0 && c16 < G) {
-      mg.m[w][c16] = m_run;
+      mg.m[w][c16] = m_ref;
       mg.l[w][c16] = lsum;
     }
 #pragma unroll
@@ -569,7 +580,6 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   __syncthreads();
   MergeLds<G>& mg = sh.merge;
   const bool single = nsplit_b <= 1;
-  float* part_base = ws + kPartialOffsetFloats(c.B, c.H);
   for (int e = tid; e < G * kD; e += 256) {
     const int hh = e / kD, ch = e % kD;
     float M = mg.m[0][hh];
@@ -588,41 +598,34 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     if (single) {
       out[qh * kD + ch] = (l > 0.f) ? o / l : 0.f;
     } else {
-      float* part = part_base + (qh * p.n_split + split) * kPartialFloats;
+      float* part = ws + (qh * p.n_split + split) * kPartialFloats;
       if (ch == 0) { part[0] = M; part[1] = l; }
       part[4 + ch] = o;
     }
   }
-  if (single) return;
+}
 
-  // ---- the last workgroup of this (sequence, KV head) merges the splits -----
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    int* ctr = reinterpret_cast<int*>(ws) + bh;
-    const int prev = atomicAdd(ctr, 1);
-    s_last = (prev == nsplit_b - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int e = tid; e < G * kD; e += 256) {
-    const int hh = e / kD, ch = e % kD;
-    const size_t qh = (size_t)b * p.Hq + (size_t)h * G + hh;
-    const float* part = part_base + qh * p.n_split * kPartialFloats;
-    float M = -INFINITY;
-    for (int s2 = 0; s2 < nsplit_b; ++s2) M = fmaxf(M, part[s2 * kPartialFloats]);
-    float o = 0.f, l = 0.f;
-    if (M != -INFINITY) {
-      for (int s2 = 0; s2 < nsplit_b; ++s2) {
-        const float f = __builtin_amdgcn_exp2f(part[s2 * kPartialFloats] - M);
-        o += f * part[s2 * kPartialFloats + 4 + ch];
-        l += f * part[s2 * kPartialFloats + 1];
-      }
+// Log-sum-exp merge of the split partials of sequences that were split: one
+// workgroup per (sequence, query head), one thread per channel.
+__global__ __launch_bounds__(128) void combine_kernel(CacheView c, AttnPlan p, const float* __restrict__ ws,
+                                                      float* __restrict__ out) {
+  const int bq = blockIdx.x, ch = threadIdx.x;
+  const int b = bq / p.Hq;
+  const int L = c.seq_len[b];
+  const int ns = (L + p.tokens_per_split - 1) / p.tokens_per_split;
+  if (ns <= 1) return;  // written directly by the attention kernel
+  const float* part = ws + (size_t)bq * p.n_split * kPartialFloats;
+  float M = -INFINITY;
+  for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, part[s2 * kPartialFloats]);
+  float o = 0.f, l = 0.f;
+  if (M != -INFINITY) {
+    for (int s2 = 0; s2 < ns; ++s2) {
+      const float f = __builtin_amdgcn_exp2f(part[s2 * kPartialFloats] - M);
+      o += f * part[s2 * kPartialFloats + 4 + ch];
+      l += f * part[s2 * kPartialFloats + 1];
     }
-    out[qh * kD + ch] = (l > 0.f) ? o / l : 0.f;
   }
-  if (tid == 0) reinterpret_cast<int*>(ws)[bh] = 0;
+  out[(size_t)bq * kD + ch] = (l > 0.f) ? o / l : 0.f;
 }
 
 template <int KB, int VB, int KAXIS, int G, bool SPARSE>
@@ -668,12 +671,16 @@ hipError_t dispatch_vb(const CacheView& c, const AttnPlan& p, const uint16_t* q,
 
 hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out,
                                    float* ws, hipStream_t st) {
+  hipError_t e;
   switch (c.kbits) {
-    case 8: return dispatch_vb<8>(c, p, q, out, ws, st);
-    case 4: return dispatch_vb<4>(c, p, q, out, ws, st);
-    case 2: return dispatch_vb<2>(c, p, q, out, ws, st);
+    case 8: e = dispatch_vb<8>(c, p, q, out, ws, st); break;
+    case 4: e = dispatch_vb<4>(c, p, q, out, ws, st); break;
+    case 2: e = dispatch_vb<2>(c, p, q, out, ws, st); break;
+    default: return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
+  if (e != hipSuccess || p.n_split <= 1) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3(c.B * p.Hq), dim3(kD), 0, st, c, p, ws, out);
+  return hipGetLastError();
 }
 
 }  // namespace kvq

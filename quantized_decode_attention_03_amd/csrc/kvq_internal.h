@@ -53,14 +53,10 @@ hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p,
                                    const uint16_t* q, float* out, float* ws,
                                    hipStream_t st);
 
-// Workspace: int32 split counters [B][H] (zero between calls), padded to 256
-// bytes, then fp32 partials [B][Hq][n_split][kPartialFloats] = m, l, 2 pad,
+// Workspace: fp32 partials [B][Hq][n_split][kPartialFloats] = m, l, 2 pad,
 // o[128].
 constexpr int kPartialFloats = 4 + kD;
 constexpr int kMinSplitTokens = 256;
-__host__ __device__ inline size_t kPartialOffsetFloats(int B, int H) {
-  return ((size_t)B * H + 63) / 64 * 64;
-}
 // Upper bound on splits per (sequence, KV head) for a given capacity.
 inline int max_splits_for(int max_tokens) {
   return (max_tokens + kMinSplitTokens - 1) / kMinSplitTokens;

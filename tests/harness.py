@@ -54,7 +54,7 @@ class Pair:
         s = self.s
         scale = 1.0 / math.sqrt(s.d_head) if scale is None else scale
         out = torch.empty((self.B, s.n_q_heads, s.d_head), dtype=torch.float32, device="cuda")
-        ws = torch.zeros(max(1, self.K.kvq_workspace_bytes(self.gpu.cfg, self.B, self.T)),
+        ws = torch.empty(max(1, self.K.kvq_workspace_bytes(self.gpu.cfg, self.B, self.T)),
                          dtype=torch.uint8, device="cuda")
         self.K.kvq_decode_attention(self.gpu, to_dev(q), out, scale, ws)
         torch.cuda.synchronize()
