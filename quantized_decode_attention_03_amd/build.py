@@ -4,7 +4,8 @@
 
 Every HIP source under csrc/ is compiled into one shared library next to this
 file. Flags: correctly rounded fp32 division (the quantizer's divisions must be
-IEEE), no fast-math, and packed-fp32 instructions disabled.
+IEEE), no fast-math, packed-fp32 instructions disabled, and MFMA
+accumulators kept in VGPRs.
 """
 import glob
 import os
@@ -22,6 +23,8 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # MFMA accumulators in ordinary VGPRs (no AGPR copies around each MFMA)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -32,6 +32,21 @@ kvq_status after_launch(hipError_t e, hipStream_t st) {
 
 bool bits_ok(int b) { return b == 2 || b == 4 || b == 8; }
 
+// Compute units of the current device (read once per device; 256 if the
+// query fails).
+int compute_units() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 kvq_status check_config(const kvq_config* cfg) {
   if (!cfg) return KVQ_EINVAL;
   if (cfg->n_kv_heads < 1 || cfg->n_q_heads < 1) return KVQ_EINVAL;
@@ -198,10 +213,11 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   p.Hq = cfg->n_q_heads;
   p.group = cfg->n_q_heads / cfg->n_kv_heads;
   p.scale = softmax_scale;
-  // tokens per split: about 1024 workgroups over all (sequence, KV head)
-  // pairs, each at least 256 and at most 2048 tokens (bounds the imbalance of
-  // ragged lengths), a multiple of 32
-  int64_t per = (total * cfg->n_kv_heads + 1023) / 1024;
+  // tokens per split: about two workgroups per compute unit over all
+  // (sequence, KV head) pairs, each at least 256 and at most 2048 tokens
+  // (bounds the imbalance of ragged lengths), a multiple of 32
+  const int64_t target = 2 * (int64_t)compute_units();
+  int64_t per = (total * cfg->n_kv_heads + target - 1) / target;
   per = std::min<int64_t>(std::max<int64_t>(per, kMinSplitTokens), 2048);
   per = (per + kBlock - 1) / kBlock * kBlock;
   p.tokens_per_split = (int)per;

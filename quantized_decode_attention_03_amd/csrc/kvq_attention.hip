@@ -77,23 +77,33 @@ __device__ __forceinline__ float trunc16(float a) {
   return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) & 0xFFFFE000u);
 }
 
+// A 32-bit constant held in a VGPR (opaque to the compiler), so that
+// (x & mask) | magic can issue as one v_and_or_b32 (gfx9 VOP3 takes no
+// literal operands).
+__device__ __forceinline__ uint32_t vconst(uint32_t x) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(x));
+  return r;
+}
+
 // 8 codes of BITS bits -> 4 fp16 pairs (magic|code) - sub[p].
 // BITS 4: lo holds 8 nibbles; pair p = (nibble p, nibble p+4).
 // BITS 2: lo holds 8 two-bit fields in its byte lane `half`*2, *2+1; pair p =
 //         (field p, field p+4).
 // BITS 8: lo, hi hold 8 bytes; pair p = (byte 2p, byte 2p+1).
+// mask: 0x000F000F (BITS 4) or 0x00030003 (BITS 2), in a VGPR.
 // magic_b: for BITS 8, the magic's high byte replicated in all four bytes.
 template <int BITS>
-__device__ __forceinline__ Frag unpack8(uint32_t lo, uint32_t hi, int half, uint32_t magic,
-                                        uint32_t magic_b, const uint32_t* sub) {
+__device__ __forceinline__ Frag unpack8(uint32_t lo, uint32_t hi, int half, uint32_t mask,
+                                        uint32_t magic, uint32_t magic_b, const uint32_t* sub) {
   Frag f;
   if constexpr (BITS == 4) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) f.p[p] = hsub2(((lo >> (4 * p)) & 0x000F000Fu) | magic, sub[p]);
+    for (int p = 0; p < 4; ++p) f.p[p] = hsub2(((lo >> (4 * p)) & mask) | magic, sub[p]);
   } else if constexpr (BITS == 2) {
     const uint32_t sp = half ? perm(0u, lo, 0x0C030C02u) : perm(0u, lo, 0x0C010C00u);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) f.p[p] = hsub2(((sp >> (2 * p)) & 0x00030003u) | magic, sub[p]);
+    for (int p = 0; p < 4; ++p) f.p[p] = hsub2(((sp >> (2 * p)) & mask) | magic, sub[p]);
   } else {
     f.p[0] = hsub2(perm(magic_b, lo, 0x04010400u), sub[0]);
     f.p[1] = hsub2(perm(magic_b, lo, 0x04030402u), sub[1]);
@@ -103,114 +113,51 @@ __device__ __forceinline__ Frag unpack8(uint32_t lo, uint32_t hi, int half, uint
   return f;
 }
 
-// Per-lane registers of one 32-token tile (quantized keys).
+// Geometry of one 32-token tile as staged in LDS:
+//   [key codes 32 x 16*KB][value block 128 x 4*VB][value meta 32 words]
+//   [key meta: 128 words (channel axis) or 32 (token axis)][sparse 32 x 2 words]
+// Key codes and the value block are contiguous in global memory and move
+// with 1 KiB direct-to-LDS loads (64 lanes x 16 bytes); the metadata pieces
+// move together in one more load whose lanes gather 16-byte chunks.
 template <int KB, int VB, int KAXIS, bool SPARSE>
-struct Tile {
-  uint32_t k[2][KB];       // key codes of the two 16-token MFMA row blocks
-  uint32_t v[8][VB == 8 ? 2 : 1];  // value codes per 16-channel chunk
-  uint32_t vm[8];          // value meta of this lane's 8 output tokens
-  uint32_t km[KAXIS ? 2 : 10];  // channel axis: meta of the lane's 2 build channels;
-                                // token axis: 8 output-token metas + 2 A-row metas
-  uint32_t sp[SPARSE ? 16 : 1];
+struct Geom {
+  static constexpr int kRowK = 16 * KB;               // key code bytes per token
+  static constexpr int kK = 32 * kRowK;               // key codes of a tile
+  static constexpr int kV = 512 * VB;                 // value block
+  static constexpr int kVm = 128;
+  static constexpr int kKm = KAXIS ? 512 : 128;
+  static constexpr int kSp = SPARSE ? 256 : 0;
+  static constexpr int kMetaLanes = (kVm + kKm + kSp) / 16;
+  static constexpr int kBytes = kK + kV + kVm + kKm + kSp;
+  static constexpr int kLoads = kK / 1024 + kV / 1024 + 1;   // DMA instructions per tile
+  // tile slots per wavefront: as many as fit 19.5 KiB, so that two 4-wave
+  // workgroups share one CU's 160 KiB of LDS
+  static constexpr int kWaveLds = KAXIS ? (4 * 17 * 4 * 16 + 4 * 4 * 4 * 4) : 0;
+  static constexpr int kSlotsFit = (19968 - kWaveLds) / kBytes;
+  static constexpr int kSlots = kSlotsFit < 2 ? 2 : (kSlotsFit > 4 ? 4 : kSlotsFit);
+  static_assert(kK % 1024 == 0 && kV % 1024 == 0, "1 KiB load granularity");
+  static_assert(kMetaLanes <= 64, "metadata fits one load");
 };
 
-template <int KB, int VB, int KAXIS, int G, bool SPARSE>
-struct Attn {
-  using T = Tile<KB, VB, KAXIS, SPARSE>;
-  static constexpr int kQMinK = -(1 << (KB - 1));
-  static constexpr int kQMinV = -(1 << (VB - 1));
-  static constexpr bool kPermK = KB != 8;  // k-slot pairs (i, i+4) for 4/2-bit keys
-  static constexpr bool kPermV = VB != 8;
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16*lane
+// (gfx950 global_load_lds_dwordx4). Issued from inline assembly so that the
+// compiler neither waits on it at every LDS read nor keeps stale LDS values
+// across it; completion is awaited explicitly with wait_vm().
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
 
-  // Lane's position in the MFMA layouts.
-  int lane, c16, grp;
-  const CacheView& c;
-  size_t bh;
-  int Q;  // quantized key tokens of the sequence
-
-  __device__ Attn(const CacheView& cv, size_t bh_, int Q_) : c(cv), bh(bh_), Q(Q_) {
-    lane = threadIdx.x & 63;
-    c16 = lane & 15;
-    grp = lane >> 4;
-  }
-
-  // Token (0..31 within the tile) of A row m in MFMA row block e.
-  __device__ static int a_token(int e, int m) { return 8 * (m >> 2) + 4 * e + (m & 3); }
-
-  __device__ void load(T& t, int t0) const {
-    // key codes: rows a_token(e, c16), bytes [grp*4*KB, +4*KB) of the row
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const uint8_t* row = c.k_codes + (bh * c.T + t0 + a_token(e, c16)) * (size_t)(16 * KB) + grp * 4 * KB;
-      if constexpr (KB == 4) {
-        const uint4 x = *reinterpret_cast<const uint4*>(row);
-        t.k[e][0] = x.x; t.k[e][1] = x.y; t.k[e][2] = x.z; t.k[e][3] = x.w;
-      } else if constexpr (KB == 8) {
-        const uint4 x = reinterpret_cast<const uint4*>(row)[0];
-        const uint4 y = reinterpret_cast<const uint4*>(row)[1];
-        t.k[e][0] = x.x; t.k[e][1] = x.y; t.k[e][2] = x.z; t.k[e][3] = x.w;
-        t.k[e][4] = y.x; t.k[e][5] = y.y; t.k[e][6] = y.z; t.k[e][7] = y.w;
-      } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(row);
-        t.k[e][0] = x.x; t.k[e][1] = x.y;
-      }
-    }
-    // value codes: channel 16j + c16, tokens 8grp .. 8grp+7 of the block
-    const uint8_t* vblk = c.v_codes + (bh * (c.T / kBlock) + t0 / kBlock) * (size_t)(kD * 4 * VB);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint8_t* rec = vblk + (16 * j + c16) * 4 * VB;
-      if constexpr (VB == 4) {
-        t.v[j][0] = reinterpret_cast<const uint32_t*>(rec)[grp];
-      } else if constexpr (VB == 8) {
-        const uint2 x = reinterpret_cast<const uint2*>(rec)[grp];
-        t.v[j][0] = x.x; t.v[j][1] = x.y;
-      } else {
-        t.v[j][0] = reinterpret_cast<const uint16_t*>(rec)[grp];
-      }
-    }
-    {
-      const uint4* vm = reinterpret_cast<const uint4*>(c.v_meta + bh * c.T + t0 + 8 * grp);
-      const uint4 a = vm[0], b = vm[1];
-      t.vm[0] = a.x; t.vm[1] = a.y; t.vm[2] = a.z; t.vm[3] = a.w;
-      t.vm[4] = b.x; t.vm[5] = b.y; t.vm[6] = b.z; t.vm[7] = b.w;
-    }
-    if constexpr (KAXIS) {
-      const uint32_t* mb = c.k_meta + (bh * (c.T / kBlock) + t0 / kBlock) * kD;
-      int c0, c1;
-      build_channels(c0, c1);
-      t.km[0] = mb[c0];
-      t.km[1] = mb[c1];
-    } else {
-      const uint4* km = reinterpret_cast<const uint4*>(c.k_meta + bh * c.T + t0 + 8 * grp);
-      const uint4 a = km[0], b = km[1];
-      t.km[0] = a.x; t.km[1] = a.y; t.km[2] = a.z; t.km[3] = a.w;
-      t.km[4] = b.x; t.km[5] = b.y; t.km[6] = b.z; t.km[7] = b.w;
-      t.km[8] = c.k_meta[bh * c.T + t0 + a_token(0, c16)];
-      t.km[9] = c.k_meta[bh * c.T + t0 + a_token(1, c16)];
-    }
-    if constexpr (SPARSE) {
-      const uint4* sp = reinterpret_cast<const uint4*>(c.k_sparse + (bh * c.T + t0 + 8 * grp) * 2);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 x = sp[i];
-        t.sp[4 * i] = x.x; t.sp[4 * i + 1] = x.y; t.sp[4 * i + 2] = x.z; t.sp[4 * i + 3] = x.w;
-      }
-    }
-  }
-
-  // Channels whose scaled query this lane builds: slot pair p of octet q.
-  __device__ void build_channels(int& c0, int& c1) const {
-    const int q = lane >> 2, p = lane & 3;
-    if (kPermK) { c0 = 8 * q + p; c1 = c0 + 4; }
-    else { c0 = 8 * q + 2 * p; c1 = c0 + 1; }
-  }
-};
-
-// LDS per wavefront: the B operand of the key product for the current block
-// (hi rows 0..G-1, lo rows G..2G-1, an all-zero row 2G; [grp][row][chunk]
-// fragments) and the per-channel subtrahends of the A operand
-// ([grp][chunk][pair]).
+// LDS per wavefront for channel-axis keys: the B operand of the key product
+// for the current block (hi rows 0..G-1, lo rows G..2G-1, an all-zero row 2G;
+// [grp][row][chunk] fragments) and the per-channel subtrahends of the A
+// operand ([grp][chunk][pair]).
 struct WaveLds {
   Frag qb[4][17][4];
   uint32_t zc[4][4][4];
@@ -239,15 +186,26 @@ __device__ __forceinline__ float grp_sum(float v) {
 // no rescaling; weights stay <= 2^kLazy.
 constexpr float kLazy = 8.f;
 
+// Token (0..31 within the tile) of A row m in MFMA row block e: row block e
+// holds tokens 8*(m/4) + 4e + m%4, so the output lane group g ends up with
+// the 8 consecutive tokens 8g..8g+7, the k-slots of its P operand.
+__device__ __forceinline__ int a_token(int e, int m) { return 8 * (m >> 2) + 4 * e + (m & 3); }
+
 template <int KB, int VB, int KAXIS, int G, bool SPARSE>
 __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, const uint16_t* __restrict__ q,
                                                    float* __restrict__ out, float* __restrict__ ws) {
-  using A = Attn<KB, VB, KAXIS, G, SPARSE>;
-  using T = typename A::T;
+  using Gm = Geom<KB, VB, KAXIS, SPARSE>;
+  constexpr int NB = Gm::kSlots;
+  constexpr int kQMinK = -(1 << (KB - 1));
+  constexpr int kQMinV = -(1 << (VB - 1));
+  constexpr bool kPermK = KB != 8;  // k-slot pairs (i, i+4) for 4/2-bit keys
+  constexpr bool kPermV = VB != 8;
   static_assert(2 * G <= 16, "hi/lo rows must fit 16");
+
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, c16 = lane & 15, grp = lane >> 4;
   const int L = c.seq_len[b];
   const int nsplit_b = (L + p.tokens_per_split - 1) / p.tokens_per_split;
   if (split > 0 && split >= nsplit_b) return;  // beyond this sequence (split 0 always runs)
@@ -255,17 +213,18 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   const int ts0 = split * p.tokens_per_split;
   const int ts1 = min(ts0 + p.tokens_per_split, L);
   const size_t bh = (size_t)b * c.H + h;
-  A at(c, bh, Q);
-  const int lane = at.lane, c16 = at.c16, grp = at.grp;
   const int hq = c16 & (G - 1);           // head of this lane's column / row
   const bool live = c16 < 2 * G;          // lanes whose column / row is used
 
-  union SharedU {
-    WaveLds wave[4];
-    MergeLds<G> merge;
-  };
-  __shared__ SharedU sh;
+  constexpr int kWaveBytes = NB * Gm::kBytes + Gm::kWaveLds;
+  constexpr int kMain = 4 * kWaveBytes;
+  constexpr int kMerge = (int)sizeof(MergeLds<G>);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kMain > kMerge ? kMain : kMerge];
   __shared__ float qsh[SPARSE ? G : 1][kD];
+
+  uint8_t* wbase = smem + w * kWaveBytes;             // this wavefront's slots
+  WaveLds& wl = *reinterpret_cast<WaveLds*>(wbase + NB * Gm::kBytes);
+  const uint32_t wbase_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)wbase;
 
   // query heads of this KV head, pre-scaled by softmax_scale * log2(e)
   const float qscale = p.scale * kLog2e;
@@ -275,9 +234,14 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     __syncthreads();
   }
 
-  WaveLds& wl = sh.wave[w];
   // channel axis: this lane builds the scaled query of 2 channels, all heads
+  // (slot pair p of octet q: channels (p, p+4) for 4/2-bit keys, (2p, 2p+1) for 8-bit)
   int bc0 = 0, bc1 = 0;
+  {
+    const int oq = lane >> 2, op = lane & 3;
+    bc0 = kPermK ? 8 * oq + op : 8 * oq + 2 * op;
+    bc1 = kPermK ? bc0 + 4 : bc0 + 1;
+  }
   float qv0[G], qv1[G];
   // token axis: the B operand is the raw fp16 query (exact), column n = head n mod G
   Frag qfrag[KAXIS ? 1 : 4];
@@ -285,7 +249,6 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   const int brow_hi = live ? hq : 2 * G;
   const int brow_lo = live ? G + hq : 2 * G;
   if constexpr (KAXIS) {
-    at.build_channels(bc0, bc1);
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       qv0[hh] = h2f(qg[hh * kD + bc0]) * qscale;
@@ -300,8 +263,8 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
         uint32_t v = 0;
         if (live) {
           const int base = 32 * grp + 8 * j;
-          const int ch0 = A::kPermK ? base + pp : base + 2 * pp;
-          const int ch1 = A::kPermK ? ch0 + 4 : ch0 + 1;
+          const int ch0 = kPermK ? base + pp : base + 2 * pp;
+          const int ch1 = kPermK ? ch0 + 4 : ch0 + 1;
           v = (uint32_t)qg[hq * kD + ch0] | ((uint32_t)qg[hq * kD + ch1] << 16);
         }
         qfrag[j].p[pp] = v;
@@ -312,35 +275,43 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   // This wavefront's tiles: k = w, w + 4, ... over [ts0, ts1).
   const int ntiles = (ts1 - ts0 + kBlock - 1) / kBlock;
   const int tq = (Q > ts0) ? min((Q - ts0 + kBlock - 1) / kBlock, ntiles) : 0;  // quantized tiles
+  const int nw = (w < tq) ? (tq - w + 3) / 4 : 0;                               // of them, mine
 
-  // Largest value-scale exponent over this wavefront's tiles: the magic
-  // exponent of the value operand (keeps p * s small in fp16).
-  int vx;
-  {
-    float smax = 0.f;
-    for (int k = w + 4 * (lane >> 5); k < ntiles; k += 8) {
-      const int t = ts0 + k * kBlock + (lane & 31);
-      if (t < ts1) smax = fmaxf(smax, h2f((uint16_t)(c.v_meta[bh * c.T + t] & 0xFFFFu)));
+  // DMA of quantized tile i of this wavefront into slot `slot`.
+  auto issue = [&](int i, int slot) {
+    const int t0 = ts0 + (w + 4 * i) * kBlock;
+    const uint32_t lb = wbase_lds + slot * Gm::kBytes;
+    const uint8_t* kg = c.k_codes + (bh * c.T + t0) * (size_t)Gm::kRowK + lane * 16;
+#pragma unroll
+    for (int x = 0; x < Gm::kK / 1024; ++x) dma16(kg + x * 1024, lb + x * 1024);
+    const uint8_t* vg = c.v_codes + (bh * (c.T / kBlock) + t0 / kBlock) * (size_t)Gm::kV + lane * 16;
+#pragma unroll
+    for (int x = 0; x < Gm::kV / 1024; ++x) dma16(vg + x * 1024, lb + Gm::kK + x * 1024);
+    if (lane < Gm::kMetaLanes) {
+      const uint8_t* mg;
+      if (lane < 8) {
+        mg = reinterpret_cast<const uint8_t*>(c.v_meta + bh * c.T + t0) + lane * 16;
+      } else if (lane < 8 + Gm::kKm / 16) {
+        const uint32_t* km = KAXIS ? c.k_meta + (bh * (c.T / kBlock) + t0 / kBlock) * kD
+                                   : c.k_meta + bh * c.T + t0;
+        mg = reinterpret_cast<const uint8_t*>(km) + (lane - 8) * 16;
+      } else {
+        mg = reinterpret_cast<const uint8_t*>(c.k_sparse + (bh * c.T + t0) * 2) +
+             (lane - 8 - Gm::kKm / 16) * 16;
+      }
+      dma16(mg, lb + Gm::kK + Gm::kV);
     }
-    smax = fmaxf(smax, __shfl_xor(smax, 1, 64));
-    smax = fmaxf(smax, __shfl_xor(smax, 2, 64));
-    smax = fmaxf(smax, __shfl_xor(smax, 4, 64));
-    smax = fmaxf(smax, __shfl_xor(smax, 8, 64));
-    smax = grp_max(smax);
-    int e = 0;
-    if (smax > 0.f) e = ((__builtin_bit_cast(uint32_t, smax) >> 23) & 0xFF) - 127;
-    vx = __builtin_amdgcn_readfirstlane(min(max(e, -24), 5));
-  }
-  const uint32_t vmagic1 = (uint32_t)(25 + vx) << 10;
-  const uint32_t vmagic = vmagic1 | (vmagic1 << 16);
-  const uint32_t vmagic_b = (vmagic1 >> 8) * 0x01010101u;
-  const float vpow = __builtin_ldexpf(1.0f, -vx);  // s * 2^-vx < 2 for the largest s
-  const h2v vpow2 = {(_Float16)__builtin_ldexpf(1.0f, vx), (_Float16)__builtin_ldexpf(1.0f, vx)};
-  const h2v vofs2 = {(_Float16)(1024 - A::kQMinV), (_Float16)(1024 - A::kQMinV)};
+  };
+
+  const h2v vofs2 = {(_Float16)(1024 - kQMinV), (_Float16)(1024 - kQMinV)};
+  const h2v kofs2 = {(_Float16)(1024 - kQMinK), (_Float16)(1024 - kQMinK)};
+  const uint32_t kmask = vconst(KB == 2 ? 0x00030003u : 0x000F000Fu);
+  const uint32_t vmask = vconst(VB == 2 ? 0x00030003u : 0x000F000Fu);
+  const uint32_t kmagic = vconst(kMagic1024);
 
   // row factors of the P operand: hi rows (c16 < G) keep p*s, lo rows take the
   // residual p*s - rtz16(p*s), rows >= 2G are zero
-  const float rowkeep = live ? vpow : 0.f;
+  const float rowkeep = live ? 1.f : 0.f;
   const float rowlo = (c16 >= G && live) ? 1.f : 0.f;
 
   float m_ref = -INFINITY, l_run = 0.f;
@@ -348,9 +319,11 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
 
-  // ---- one tile: scores -> online softmax -> P.V -------------------------
-  auto softmax_pv = [&](float (&sc)[8], const T& t, int t0) {
-    // sc[4e + r] is the score of token 8grp + 4e + r (log2 units)
+  // ---- scores of one tile -> online softmax -> P.V ---------------------------
+  // sc[4e + r] is the score of token 8grp + 4e + r (log2 units); vm[i] the value
+  // meta of token 8grp + i; vcode(j) gives the lane's value codes of chunk j.
+  auto softmax_pv = [&](float (&sc)[8], const uint32_t (&vm)[8], const uint32_t (&vcl)[8],
+                        const uint32_t (&vch)[8], int t0) {
     const int nvalid = ts1 - t0;
     float mx = -INFINITY;
 #pragma unroll
@@ -371,167 +344,216 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
       l_run *= alpha;
       m_ref = m_new;
     }
-    float pr[8];
+    // Magic exponent vx of this lane group's value operand: the largest of its
+    // 8 value scales is brought to [1, 2) in P = p * s * 2^-vx, and the value
+    // codes carry the 2^vx back (B = (u - z') * 2^vx), so the product is
+    // unchanged; k-slots of one lane group meet only each other in the MFMA.
+    float sv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_ref);
-      l_run += pr[i];
-    }
-    // P operand (k-slot order of the value codes) and value subtrahends
-    Frag pf;
-    uint32_t vsub[4];
+    for (int i = 0; i < 8; ++i) sv[i] = h2f((uint16_t)(vm[i] & 0xFFFFu));
+    const float smax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                             fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    const int ex = (smax > 0.f) ? (int)((__builtin_bit_cast(uint32_t, smax) >> 23) & 0xFF) - 127 : 0;
+    const int vx = min(max(ex, -24), 5);
+    const uint32_t vmagic1 = (uint32_t)(25 + vx) << 10;
+    const uint32_t vmagic = vmagic1 * 0x10001u;
+    const uint32_t vmagic_b = (vmagic1 >> 8) * 0x01010101u;
+    const float vpow = __builtin_ldexpf(rowkeep, -vx);
+    const uint32_t p2 = (vx >= -14) ? (uint32_t)(vx + 15) << 10 : 1u << (vx + 24);  // fp16 2^vx
+    const h2v vpow2 = as_h2(p2 * 0x10001u);
     float pv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float x = pr[i] * (h2f((uint16_t)(t.vm[i] & 0xFFFFu)) * rowkeep);
+      const float pr = __builtin_amdgcn_exp2f(sc[i] - m_ref);
+      l_run += pr;
+      const float x = pr * (sv[i] * vpow);
       pv[i] = x - rowlo * trunc16(x);
     }
+    Frag pf;
+    uint32_t vsub[4];
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      const int i0 = A::kPermV ? pp : 2 * pp;
-      const int i1 = A::kPermV ? pp + 4 : 2 * pp + 1;
+      const int i0 = kPermV ? pp : 2 * pp;
+      const int i1 = kPermV ? pp + 4 : 2 * pp + 1;
       pf.p[pp] = pk_rtz(pv[i0], pv[i1]);
-      const uint32_t zz = perm(t.vm[i1], t.vm[i0], 0x07060302u);  // (z_i0, z_i1)
+      const uint32_t zz = perm(vm[i1], vm[i0], 0x07060302u);  // (z_i0, z_i1)
       vsub[pp] = as_u32((as_h2(zz) + vofs2) * vpow2);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const Frag vf = unpack8<VB>(t.v[j][0], VB == 8 ? t.v[j][VB == 8 ? 1 : 0] : 0u, 0, vmagic,
-                                  vmagic_b, vsub);
+      const Frag vf = unpack8<VB>(vcl[j], vch[j], 0, vmask, vmagic, vmagic_b, vsub);
       acc[j] = mfma(pf, vf, acc[j]);
     }
   };
 
-  // key product of one tile; fills sc[8]
-  auto qk_quant = [&](const T& t, float (&sc)[8]) {
-    f4v s[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
-    if constexpr (KAXIS) {
-      // B operand (scaled query, hi/lo) and A subtrahends of this block
-      {
-        const float s0 = h2f((uint16_t)(t.km[0] & 0xFFFFu)), s1 = h2f((uint16_t)(t.km[1] & 0xFFFFu));
-        const int bq = lane >> 2, bp = lane & 3, bg = bq >> 2, bj = bq & 3;
-        wave_lds_fence();
+  // the B operand of the key product for a block: scaled query (hi/lo) with
+  // per-channel scales s0, s1 of this lane's two build channels
+  auto build_qb = [&](float s0, float s1, uint32_t km0, uint32_t km1, bool with_zero) {
+    const int bq = lane >> 2, bp = lane & 3, bg = bq >> 2, bj = bq & 3;
+    wave_lds_fence();
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const float v0 = qv0[hh] * s0, v1 = qv1[hh] * s1;
-          wl.qb[bg][hh][bj].p[bp] = pk_rtz(v0, v1);
-          wl.qb[bg][G + hh][bj].p[bp] = pk_rtz(v0 - trunc16(v0), v1 - trunc16(v1));
-        }
-        const uint32_t zz = perm(t.km[1], t.km[0], 0x07060302u);
-        const h2v kofs = {(_Float16)(1024 - A::kQMinK), (_Float16)(1024 - A::kQMinK)};
-        wl.zc[bg][bj][bp] = as_u32(as_h2(zz) + kofs);
-        wave_lds_fence();
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const Frag qh = wl.qb[grp][brow_hi][j];
-        const Frag ql = wl.qb[grp][brow_lo][j];
-        uint32_t zsub[4];
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) zsub[pp] = wl.zc[grp][j][pp];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          Frag kf;
-          if constexpr (KB == 4) kf = unpack8<4>(t.k[e][j], 0u, 0, kMagic1024, 0u, zsub);
-          else if constexpr (KB == 8) kf = unpack8<8>(t.k[e][2 * j], t.k[e][2 * j + 1], 0, kMagic1024, 0x64646464u, zsub);
-          else kf = unpack8<2>(t.k[e][j >> 1], 0u, j & 1, kMagic1024, 0u, zsub);
-          s[e] = mfma(kf, qh, s[e]);
-          s[e] = mfma(kf, ql, s[e]);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[4 * e + r] = s[e][r];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint32_t zt = (t.km[8 + e] >> 16) | (t.km[8 + e] & 0xFFFF0000u);  // (z, z)
-        const h2v kofs = {(_Float16)(1024 - A::kQMinK), (_Float16)(1024 - A::kQMinK)};
-        const uint32_t zs = as_u32(as_h2(zt) + kofs);
-        const uint32_t zsub[4] = {zs, zs, zs, zs};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          Frag kf;
-          if constexpr (KB == 4) kf = unpack8<4>(t.k[e][j], 0u, 0, kMagic1024, 0u, zsub);
-          else if constexpr (KB == 8) kf = unpack8<8>(t.k[e][2 * j], t.k[e][2 * j + 1], 0, kMagic1024, 0x64646464u, zsub);
-          else kf = unpack8<2>(t.k[e][j >> 1], 0u, j & 1, kMagic1024, 0u, zsub);
-          s[e] = mfma(kf, qfrag[j], s[e]);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sc[4 * e + r] = s[e][r] * (h2f((uint16_t)(t.km[4 * e + r] & 0xFFFFu)) * qscale);
+    for (int hh = 0; hh < G; ++hh) {
+      const float v0 = qv0[hh] * s0, v1 = qv1[hh] * s1;
+      wl.qb[bg][hh][bj].p[bp] = pk_rtz(v0, v1);
+      wl.qb[bg][G + hh][bj].p[bp] = pk_rtz(v0 - trunc16(v0), v1 - trunc16(v1));
     }
-    if constexpr (SPARSE) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t sv = t.sp[2 * i], scol = t.sp[2 * i + 1];
-        sc[i] += qsh[hq][scol & 0xFFFFu] * h2f((uint16_t)(sv & 0xFFFFu)) +
-                 qsh[hq][scol >> 16] * h2f((uint16_t)(sv >> 16));
-      }
-    }
+    if (with_zero) wl.zc[bg][bj][bp] = as_u32(as_h2(perm(km1, km0, 0x07060302u)) + kofs2);
+    wave_lds_fence();
   };
 
-  // ---- quantized tiles, one tile of loads in flight ahead -------------------
-  if (w < tq) {
-    T ta, tb;
-    const int klast = tq - 1 - ((tq - 1 - w) & 3);  // last tile of this wavefront
-    int k = w;
-    at.load(ta, ts0 + k * kBlock);
-    while (true) {
+  // ---- quantized tiles through the LDS pipeline -----------------------------
+  if (nw > 0) {
+#pragma unroll
+    for (int i = 0; i < NB - 1; ++i)
+      if (i < nw) issue(i, i);
+    for (int i = 0; i < nw; ++i) {
+      const int slot = i % NB;
+      if (i + NB - 1 < nw) issue(i + NB - 1, (i + NB - 1) % NB);
+      // tile i has landed once at most (tiles issued after it) x loads remain
+      switch (min(NB - 1, nw - 1 - i)) {
+        case 0: wait_vm<0>(); break;
+        case 1: wait_vm<Gm::kLoads>(); break;
+        case 2: wait_vm<(NB > 2 ? 2 : 1) * Gm::kLoads>(); break;
+        default: wait_vm<(NB > 3 ? 3 : 1) * Gm::kLoads>(); break;
+      }
+      const uint8_t* sb = wbase + slot * Gm::kBytes;
+      const uint8_t* kbuf = sb;
+      const uint8_t* vbuf = sb + Gm::kK;
+      const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(sb + Gm::kK + Gm::kV);
+      const uint32_t* kmeta = vmeta + 32;
+      const uint32_t* spr = kmeta + Gm::kKm / 4;
+      const int t0 = ts0 + (w + 4 * i) * kBlock;
+
+      uint32_t vm[8];
+      {
+        const uint4 a = reinterpret_cast<const uint4*>(vmeta + 8 * grp)[0];
+        const uint4 bb = reinterpret_cast<const uint4*>(vmeta + 8 * grp)[1];
+        vm[0] = a.x; vm[1] = a.y; vm[2] = a.z; vm[3] = a.w;
+        vm[4] = bb.x; vm[5] = bb.y; vm[6] = bb.z; vm[7] = bb.w;
+      }
+      // key codes of the lane's two A rows: bytes [grp*4KB, +4KB) of each row
+      uint32_t kc[2][KB];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint8_t* row = kbuf + a_token(e, c16) * Gm::kRowK + grp * 4 * KB;
+#pragma unroll
+        for (int x = 0; x < KB; x += 2) {
+          const uint2 y = reinterpret_cast<const uint2*>(row)[x / 2];
+          kc[e][x] = y.x;
+          kc[e][x + 1] = y.y;
+        }
+      }
       float sc[8];
-      at.load(tb, ts0 + min(k + 4, klast) * kBlock);
-      qk_quant(ta, sc);
-      softmax_pv(sc, ta, ts0 + k * kBlock);
-      k += 4;
-      if (k > klast) break;
-      at.load(ta, ts0 + min(k + 4, klast) * kBlock);
-      qk_quant(tb, sc);
-      softmax_pv(sc, tb, ts0 + k * kBlock);
-      k += 4;
-      if (k > klast) break;
+      f4v s[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
+      if constexpr (KAXIS) {
+        const uint32_t km0 = kmeta[bc0], km1 = kmeta[bc1];
+        build_qb(h2f((uint16_t)(km0 & 0xFFFFu)), h2f((uint16_t)(km1 & 0xFFFFu)), km0, km1, true);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const Frag qh = wl.qb[grp][brow_hi][j];
+          const Frag ql = wl.qb[grp][brow_lo][j];
+          uint32_t zsub[4];
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) zsub[pp] = wl.zc[grp][j][pp];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            Frag kf;
+            if constexpr (KB == 4) kf = unpack8<4>(kc[e][j], 0u, 0, kmask, kmagic, 0u, zsub);
+            else if constexpr (KB == 8) kf = unpack8<8>(kc[e][2 * j], kc[e][2 * j + 1], 0, kmask, kmagic, 0x64646464u, zsub);
+            else kf = unpack8<2>(kc[e][j >> 1], 0u, j & 1, kmask, kmagic, 0u, zsub);
+            s[e] = mfma(kf, qh, s[e]);
+            s[e] = mfma(kf, ql, s[e]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[4 * e + r] = s[e][r];
+      } else {
+        uint32_t km[8];
+        {
+          const uint4 a = reinterpret_cast<const uint4*>(kmeta + 8 * grp)[0];
+          const uint4 bb = reinterpret_cast<const uint4*>(kmeta + 8 * grp)[1];
+          km[0] = a.x; km[1] = a.y; km[2] = a.z; km[3] = a.w;
+          km[4] = bb.x; km[5] = bb.y; km[6] = bb.z; km[7] = bb.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t ka = kmeta[a_token(e, c16)];
+          const uint32_t zt = (ka >> 16) | (ka & 0xFFFF0000u);  // (z, z)
+          const uint32_t zs = as_u32(as_h2(zt) + kofs2);
+          const uint32_t zsub[4] = {zs, zs, zs, zs};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            Frag kf;
+            if constexpr (KB == 4) kf = unpack8<4>(kc[e][j], 0u, 0, kmask, kmagic, 0u, zsub);
+            else if constexpr (KB == 8) kf = unpack8<8>(kc[e][2 * j], kc[e][2 * j + 1], 0, kmask, kmagic, 0x64646464u, zsub);
+            else kf = unpack8<2>(kc[e][j >> 1], 0u, j & 1, kmask, kmagic, 0u, zsub);
+            s[e] = mfma(kf, qfrag[j], s[e]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sc[4 * e + r] = s[e][r] * (h2f((uint16_t)(km[4 * e + r] & 0xFFFFu)) * qscale);
+      }
+      if constexpr (SPARSE) {
+#pragma unroll
+        for (int i2 = 0; i2 < 8; ++i2) {
+          const uint2 rec = reinterpret_cast<const uint2*>(spr)[8 * grp + i2];
+          sc[i2] += qsh[hq][rec.y & 0xFFFFu] * h2f((uint16_t)(rec.x & 0xFFFFu)) +
+                    qsh[hq][rec.y >> 16] * h2f((uint16_t)(rec.x >> 16));
+        }
+      }
+      // value codes: channel 16j + c16, tokens 8grp .. 8grp+7 of the block
+      uint32_t vcl[8], vch[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint8_t* rec = vbuf + (16 * j + c16) * 4 * VB;
+        if constexpr (VB == 4) {
+          vcl[j] = reinterpret_cast<const uint32_t*>(rec)[grp];
+          vch[j] = 0u;
+        } else if constexpr (VB == 8) {
+          const uint2 x = reinterpret_cast<const uint2*>(rec)[grp];
+          vcl[j] = x.x;
+          vch[j] = x.y;
+        } else {
+          vcl[j] = reinterpret_cast<const uint16_t*>(rec)[grp];
+          vch[j] = 0u;
+        }
+      }
+      softmax_pv(sc, vm, vcl, vch, t0);
     }
   }
+
   // ---- residual (fp16) key tiles: channel axis only ------------------------
   if constexpr (KAXIS) {
     for (int k = tq + ((w - tq) % 4 + 4) % 4; k < ntiles; k += 4) {
       const int t0 = ts0 + k * kBlock;
-      T t;
+      uint32_t vm[8], vcl[8], vch[8];
       {
-        const uint8_t* vblk = c.v_codes + (bh * (c.T / kBlock) + t0 / kBlock) * (size_t)(kD * 4 * VB);
+        const uint8_t* vblk = c.v_codes + (bh * (c.T / kBlock) + t0 / kBlock) * (size_t)Gm::kV;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const uint8_t* rec = vblk + (16 * j + c16) * 4 * VB;
-          if constexpr (VB == 4) t.v[j][0] = reinterpret_cast<const uint32_t*>(rec)[grp];
+          if constexpr (VB == 4) { vcl[j] = reinterpret_cast<const uint32_t*>(rec)[grp]; vch[j] = 0u; }
           else if constexpr (VB == 8) {
             const uint2 x = reinterpret_cast<const uint2*>(rec)[grp];
-            t.v[j][0] = x.x; t.v[j][VB == 8 ? 1 : 0] = x.y;
-          } else t.v[j][0] = reinterpret_cast<const uint16_t*>(rec)[grp];
+            vcl[j] = x.x; vch[j] = x.y;
+          } else { vcl[j] = reinterpret_cast<const uint16_t*>(rec)[grp]; vch[j] = 0u; }
         }
-        const uint4* vm = reinterpret_cast<const uint4*>(c.v_meta + bh * c.T + t0 + 8 * grp);
-        const uint4 a = vm[0], bb = vm[1];
-        t.vm[0] = a.x; t.vm[1] = a.y; t.vm[2] = a.z; t.vm[3] = a.w;
-        t.vm[4] = bb.x; t.vm[5] = bb.y; t.vm[6] = bb.z; t.vm[7] = bb.w;
+        const uint4* vmg = reinterpret_cast<const uint4*>(c.v_meta + bh * c.T + t0 + 8 * grp);
+        const uint4 a = vmg[0], bb = vmg[1];
+        vm[0] = a.x; vm[1] = a.y; vm[2] = a.z; vm[3] = a.w;
+        vm[4] = bb.x; vm[5] = bb.y; vm[6] = bb.z; vm[7] = bb.w;
       }
       // B operand: query scaled by the softmax factor only, hi/lo
-      {
-        const int bq = lane >> 2, bp = lane & 3, bg = bq >> 2, bj = bq & 3;
-        wave_lds_fence();
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const float v0 = qv0[hh], v1 = qv1[hh];
-          wl.qb[bg][hh][bj].p[bp] = pk_rtz(v0, v1);
-          wl.qb[bg][G + hh][bj].p[bp] = pk_rtz(v0 - trunc16(v0), v1 - trunc16(v1));
-        }
-        wave_lds_fence();
-      }
+      build_qb(1.f, 1.f, 0u, 0u, false);
       f4v s[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int tt = t0 + A::a_token(e, c16);
+        const int tt = t0 + a_token(e, c16);
         const bool ok = tt < ts1;
         const uint16_t* kr = c.k_resid + (bh * c.R + (ok ? tt - Q : 0)) * kD + 32 * grp;
 #pragma unroll
@@ -539,7 +561,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           uint4 x = reinterpret_cast<const uint4*>(kr + 8 * j)[0];
           if (!ok) x = make_uint4(0, 0, 0, 0);
           Frag kf;
-          if (A::kPermK) {  // pairs (channel p, p+4)
+          if (kPermK) {  // pairs (channel p, p+4)
             kf.p[0] = perm(x.z, x.x, 0x05040100u);
             kf.p[1] = perm(x.z, x.x, 0x07060302u);
             kf.p[2] = perm(x.w, x.y, 0x05040100u);
@@ -556,29 +578,26 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
       for (int e = 0; e < 2; ++e)
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[4 * e + r] = s[e][r];
-      softmax_pv(sc, t, t0);
+      softmax_pv(sc, vm, vcl, vch, t0);
     }
   }
 
   // ---- merge the wavefronts of the workgroup --------------------------------
-  {
-    const float lsum = grp_sum(l_run);
-    __syncthreads();  // every wavefront is done with its WaveLds
-    MergeLds<G>& mg = sh.merge;
-    if (grp == 0 && c16 < G) {
-      mg.m[w][c16] = m_ref;
-      mg.l[w][c16] = lsum;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * grp + r;
-        if (row < 2 * G) mg.o[w][row][16 * j + c16] = acc[j][r];
-      }
+  const float lsum = grp_sum(l_run);
+  __syncthreads();  // every wavefront is done with its slots
+  MergeLds<G>& mg = *reinterpret_cast<MergeLds<G>*>(smem);
+  if (grp == 0 && c16 < G) {
+    mg.m[w][c16] = m_ref;
+    mg.l[w][c16] = lsum;
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * grp + r;
+      if (row < 2 * G) mg.o[w][row][16 * j + c16] = acc[j][r];
+    }
   __syncthreads();
-  MergeLds<G>& mg = sh.merge;
   const bool single = nsplit_b <= 1;
   for (int e = tid; e < G * kD; e += 256) {
     const int hh = e / kD, ch = e % kD;
