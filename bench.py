@@ -47,6 +47,33 @@ def algorithmic_bytes(s, lens):
     return tot
 
 
+def attention_source_hash():
+    """Hash of the attention kernel sources; HBM traffic figures recorded under
+    profiles/ apply only while it is unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "quantized_decode_attention_03_amd", "csrc")
+    for f in ("kvq_attention.hip", "kvq_device.h", "kvq_internal.h"):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(cid):
+    """Calibrated HBM bytes per attention launch from the rocprofv3 counter runs
+    recorded in profiles/traffic.json (FETCH_SIZE and WRITE_SIZE, each scaled by
+    the same counter's reading for a plain copy of known size), or None when
+    there is no record for this workload or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(str(cid))
+    if not rec or rec.get("source_sha256_16") != attention_source_hash():
+        return None
+    return rec["traffic_bytes_per_dispatch"]
+
+
 def cpu_baseline(s, n_seq, steps):
     """The oracle's decode step (append + float64 attention) on a subset of the
     sequences, timed on the host. Returns (tokens/s, threads, description)."""
@@ -72,6 +99,29 @@ def cpu_baseline(s, n_seq, steps):
     return n_seq * steps / dt, threads, dt
 
 
+def copy_probe():
+    """A plain copy of known size: reads and writes 1 GiB per launch. Its HBM
+    counters calibrate the attention kernel's, and its rate is the attainable
+    copy bandwidth on this device."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    reps = 10
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "avg_ms": ms,
+                      "read_plus_write_GBps": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +132,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=16)
     ap.add_argument("--cpu-steps", type=int, default=8)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="time a plain 1 GiB device copy (HBM reference and counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
@@ -95,6 +147,9 @@ def main():
     from quantized_decode_attention_03_amd import _native
 
     _native.lib()
+    if args.copy_probe:
+        copy_probe()
+        return
     s = W.spec(args.config)
     if s.layers != 1:
         raise SystemExit("bench.py times single-layer workloads")
@@ -190,7 +245,7 @@ def main():
                    "k_group": s.k_group, "k_residual": s.k_residual, "k_sparse": s.k_sparse,
                    "cache_replicas": nrep},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_GBS, "traffic": None,
+                     "frac": achieved / PEAK_GBS, "traffic": recorded_traffic(args.config),
                      "kernel": "kvq_decode_attention (attention + split merge)",
                      "avg_launch_us": attn_avg_s * 1e6,
                      "p10_p90_us": [float(np.percentile(attn_ms, 10)) * 1e3,
