@@ -43,6 +43,10 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kMagic1024 = 0x64006400u;  // fp16 pair (1024, 1024)
+#ifndef KVQ_WAVE_LDS_BUDGET
+#define KVQ_WAVE_LDS_BUDGET 19968
+#endif
+constexpr int kWaveBudget = KVQ_WAVE_LDS_BUDGET;  // LDS bytes per wavefront
 
 struct Frag {  // 8 fp16 MFMA operand values as 4 packed pairs
   uint32_t p[4];
@@ -119,7 +123,7 @@ __device__ __forceinline__ Frag unpack8(uint32_t lo, uint32_t hi, int half, uint
 // Key codes and the value block are contiguous in global memory and move
 // with 1 KiB direct-to-LDS loads (64 lanes x 16 bytes); the metadata pieces
 // move together in one more load whose lanes gather 16-byte chunks.
-template <int KB, int VB, int KAXIS, bool SPARSE>
+template <int KB, int VB, int KAXIS, int G, bool SPARSE>
 struct Geom {
   static constexpr int kRowK = 16 * KB;               // key code bytes per token
   static constexpr int kK = 32 * kRowK;               // key codes of a tile
@@ -130,10 +134,12 @@ struct Geom {
   static constexpr int kMetaLanes = (kVm + kKm + kSp) / 16;
   static constexpr int kBytes = kK + kV + kVm + kKm + kSp;
   static constexpr int kLoads = kK / 1024 + kV / 1024 + 1;   // DMA instructions per tile
-  // tile slots per wavefront: as many as fit 19.5 KiB, so that two 4-wave
-  // workgroups share one CU's 160 KiB of LDS
-  static constexpr int kWaveLds = KAXIS ? (4 * 17 * 4 * 16 + 4 * 4 * 4 * 4) : 0;
-  static constexpr int kSlotsFit = (19968 - kWaveLds) / kBytes;
+  // the key-product B operand and subtrahends (channel axis only)
+  static constexpr int kWaveLds = KAXIS ? (4 * (2 * G + 1) * 4 * 16 + 4 * 4 * 4 * 4) : 0;
+  // tile slots per wavefront: as many as fit the per-wavefront LDS budget
+  // (kWaveBudget, chosen so that several 4-wavefront workgroups share a CU's
+  // 160 KiB), between 2 and 4
+  static constexpr int kSlotsFit = (kWaveBudget - kWaveLds) / kBytes;
   static constexpr int kSlots = kSlotsFit < 2 ? 2 : (kSlotsFit > 4 ? 4 : kSlotsFit);
   static_assert(kK % 1024 == 0 && kV % 1024 == 0, "1 KiB load granularity");
   static_assert(kMetaLanes <= 64, "metadata fits one load");
@@ -158,8 +164,9 @@ __device__ __forceinline__ void wait_vm() {
 // for the current block (hi rows 0..G-1, lo rows G..2G-1, an all-zero row 2G;
 // [grp][row][chunk] fragments) and the per-channel subtrahends of the A
 // operand ([grp][chunk][pair]).
+template <int G>
 struct WaveLds {
-  Frag qb[4][17][4];
+  Frag qb[4][2 * G + 1][4];
   uint32_t zc[4][4][4];
 };
 
@@ -194,7 +201,7 @@ __device__ __forceinline__ int a_token(int e, int m) { return 8 * (m >> 2) + 4 *
 template <int KB, int VB, int KAXIS, int G, bool SPARSE>
 __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, const uint16_t* __restrict__ q,
                                                    float* __restrict__ out, float* __restrict__ ws) {
-  using Gm = Geom<KB, VB, KAXIS, SPARSE>;
+  using Gm = Geom<KB, VB, KAXIS, G, SPARSE>;
   constexpr int NB = Gm::kSlots;
   constexpr int kQMinK = -(1 << (KB - 1));
   constexpr int kQMinV = -(1 << (VB - 1));
@@ -223,7 +230,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   __shared__ float qsh[SPARSE ? G : 1][kD];
 
   uint8_t* wbase = smem + w * kWaveBytes;             // this wavefront's slots
-  WaveLds& wl = *reinterpret_cast<WaveLds*>(wbase + NB * Gm::kBytes);
+  WaveLds<G>& wl = *reinterpret_cast<WaveLds<G>*>(wbase + NB * Gm::kBytes);
   const uint32_t wbase_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)wbase;
 
   // query heads of this KV head, pre-scaled by softmax_scale * log2(e)
