@@ -12,17 +12,30 @@
 // Shape of the work. The g query heads that share a KV head turn both products
 // into small dense contractions, so they run on v_mfma_f32_16x16x32_f16:
 //   S^T[token, col] = sum_c A[token, c] * B[c, col]
-//       A = dequantization-ready key codes (u - z') in fp16 (exact integers),
-//       B = query columns; for per-channel keys the per-channel scale is
-//           folded into the query (q * s_c), split into an fp16 hi and lo
-//           part placed in columns h and g + h, so the product keeps ~22 bits.
-//   O[row, c] = sum_t P[row, t] * V[t, c]
-//       P = p_t * s_t (value scale folded into the softmax weight), again as
-//           hi/lo rows h and g + h; V = value codes (u - z') in fp16.
-// Codes become fp16 by OR-ing them into the mantissa of a power of two
-// ("magic" exponent) and subtracting that power plus the zero-point in one
-// packed fp16 operation. For values the magic exponent also absorbs the
-// wavefront's largest value-scale exponent, which keeps p * s within fp16.
+//   O[row, c]       = sum_t P[row, t] * V[t, c]
+// Codes enter the matrix cores as their own bit patterns: a stored code u
+// placed at bit SH of an fp16 (u << SH < 2^10) is the subnormal u * 2^(SH-24),
+// which the matrix cores multiply exactly. Unpacking is therefore only shifts
+// and masks. SH is 8 for 2-bit codes, 4 for 4-bit and 0 for 8-bit: chains of
+// accumulating MFMAs lose accuracy when the operands are very small (measured:
+// 2-bit codes at u * 2^-24 gave key-score errors near 2e-3, at u * 2^-16 near
+// 5e-6 on the same data), so small codes sit as high in the subnormal range
+// as the shift-and-mask extraction allows. The zero points are not subtracted element by element; their
+// contribution is a rank-one term that runs on the matrix cores as well:
+//   keys, channel axis: x = s_c (u - z'_c); B = q * s_c (scaled query, split
+//     into fp16 hi and lo parts in columns h and g + h, ~22 bits); the term
+//     sum_c z'_c B[c, col] is the same for every token of a block and seeds
+//     the accumulator (an A operand whose rows all hold -z', in the same
+//     code-step units as the codes);
+//   keys, token axis: x = s_t (u - z'_t); B = raw fp16 query (exact); the
+//     term z'_t sum_c q_c seeds the accumulator the same way (row t of the A
+//     operand holds -z'_t); s_t multiplies the scores afterwards;
+//   values, token axis: x = s_t (u - z'_t); P = p_t * s_t * 2^kv as hi/lo rows
+//     h and g + h; the product with a B operand whose columns all hold z'_t
+//     is subtracted once at the end.
+// The factor 2^kv keeps p * s inside fp16: it is one exponent per wavefront,
+// raised lazily (rarely) when a larger value scale shows up, like the softmax
+// reference.
 //
 // Work split: grid (split, KV head, sequence), 4 wavefronts per workgroup,
 // each wavefront owns every 4th 32-token tile of the split and keeps its own
@@ -42,7 +55,7 @@ typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr uint32_t kMagic1024 = 0x64006400u;  // fp16 pair (1024, 1024)
+constexpr float kTwoM24 = 1.f / 16777216.f;     // 2^-24, the smallest fp16 subnormal
 #ifndef KVQ_WAVE_LDS_BUDGET
 #define KVQ_WAVE_LDS_BUDGET 19968
 #endif
@@ -54,8 +67,17 @@ struct Frag {  // 8 fp16 MFMA operand values as 4 packed pairs
 
 __device__ __forceinline__ h2v as_h2(uint32_t x) { return __builtin_bit_cast(h2v, x); }
 __device__ __forceinline__ uint32_t as_u32(h2v x) { return __builtin_bit_cast(uint32_t, x); }
-__device__ __forceinline__ uint32_t hsub2(uint32_t a, uint32_t b) {
-  return as_u32(as_h2(a) - as_h2(b));
+
+// fp16 halves of a word, widened (v_cvt or folded into a v_fma_mix_f32)
+__device__ __forceinline__ float f16lo(uint32_t w) { return (float)as_h2(w)[0]; }
+__device__ __forceinline__ float f16hi(uint32_t w) { return (float)as_h2(w)[1]; }
+// x * (fp16 low half of w) as one v_fma_mix_f32 (a -0 product comes out +0)
+__device__ __forceinline__ float mul_lo(float x, uint32_t w) { return __builtin_fmaf(x, f16lo(w), 0.f); }
+
+// fp16 pair (a * m + c, b * m + c) of the fp16 halves of w (one v_pk_fma_f16)
+__device__ __forceinline__ uint32_t pk_fma16(uint32_t w, _Float16 m, _Float16 c) {
+  const h2v mm = {m, m}, cc = {c, c};
+  return as_u32(__builtin_elementwise_fma(as_h2(w), mm, cc));
 }
 
 __device__ __forceinline__ f4v mfma(const Frag& a, const Frag& b, f4v c) {
@@ -76,45 +98,53 @@ __device__ __forceinline__ void wave_lds_fence() {
 __device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
-// a with the 13 low mantissa bits cleared: the fp16-RTZ value of a (normal range).
-__device__ __forceinline__ float trunc16(float a) {
-  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) & 0xFFFFE000u);
-}
 
-// A 32-bit constant held in a VGPR (opaque to the compiler), so that
-// (x & mask) | magic can issue as one v_and_or_b32 (gfx9 VOP3 takes no
-// literal operands).
-__device__ __forceinline__ uint32_t vconst(uint32_t x) {
-  uint32_t r;
-  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(x));
-  return r;
-}
-
-// 8 codes of BITS bits -> 4 fp16 pairs (magic|code) - sub[p].
-// BITS 4: lo holds 8 nibbles; pair p = (nibble p, nibble p+4).
-// BITS 2: lo holds 8 two-bit fields in its byte lane `half`*2, *2+1; pair p =
-//         (field p, field p+4).
-// BITS 8: lo, hi hold 8 bytes; pair p = (byte 2p, byte 2p+1).
-// mask: 0x000F000F (BITS 4) or 0x00030003 (BITS 2), in a VGPR.
-// magic_b: for BITS 8, the magic's high byte replicated in all four bytes.
+// Bit position of a code inside its fp16 operand (the code's value is
+// u * 2^(SH-24)).
 template <int BITS>
-__device__ __forceinline__ Frag unpack8(uint32_t lo, uint32_t hi, int half, uint32_t mask,
-                                        uint32_t magic, uint32_t magic_b, const uint32_t* sub) {
+constexpr int code_shift() { return BITS == 2 ? 8 : (BITS == 4 ? 4 : 0); }
+
+// Two fields of BITS bits, at bit n and n + 16 of w, moved to bit SH of each
+// half: the fp16 pair (u0 * 2^(SH-24), u1 * 2^(SH-24)).
+template <int BITS>
+__device__ __forceinline__ uint32_t field_pair(uint32_t w, int n) {
+  constexpr int SH = code_shift<BITS>();
+  constexpr uint32_t kMask = (((1u << BITS) - 1u) << SH) * 0x10001u;
+  if (n == SH) return w & kMask;
+  if (n < SH) return (w << (SH - n)) & kMask;
+  return (w >> (n - SH)) & kMask;
+}
+
+// 8 codes -> 4 fp16 code pairs, k-slot pairs (2p, 2p+1) taking:
+//   BITS 4: word a, nibbles (p, p+4);
+//   BITS 2: word a, 2-bit fields (4y + p, 4y + p + 8), y = 0 or 1;
+//   BITS 8: bytes (2p, 2p+1) of the 8 bytes a, b.
+template <int BITS>
+__device__ __forceinline__ Frag codes8(uint32_t a, uint32_t b, int y) {
   Frag f;
   if constexpr (BITS == 4) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) f.p[p] = hsub2(((lo >> (4 * p)) & mask) | magic, sub[p]);
+    for (int p = 0; p < 4; ++p) f.p[p] = field_pair<4>(a, 4 * p);
   } else if constexpr (BITS == 2) {
-    const uint32_t sp = half ? perm(0u, lo, 0x0C030C02u) : perm(0u, lo, 0x0C010C00u);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) f.p[p] = hsub2(((sp >> (2 * p)) & mask) | magic, sub[p]);
+    for (int p = 0; p < 4; ++p) f.p[p] = field_pair<2>(a, 8 * y + 2 * p);
   } else {
-    f.p[0] = hsub2(perm(magic_b, lo, 0x04010400u), sub[0]);
-    f.p[1] = hsub2(perm(magic_b, lo, 0x04030402u), sub[1]);
-    f.p[2] = hsub2(perm(magic_b, hi, 0x04010400u), sub[2]);
-    f.p[3] = hsub2(perm(magic_b, hi, 0x04030402u), sub[3]);
+    f.p[0] = perm(0u, a, 0x0C010C00u);
+    f.p[1] = perm(0u, a, 0x0C030C02u);
+    f.p[2] = perm(0u, b, 0x0C010C00u);
+    f.p[3] = perm(0u, b, 0x0C030C02u);
   }
   return f;
+}
+
+// Channel of k-slot pair p (first or second slot) in chunk j of lane group
+// grp, for key codes of BITS bits. Key rows are channel-packed with the low
+// bits first; this is the order codes8() produces.
+template <int BITS>
+__device__ __forceinline__ int key_channel(int grp, int j, int p, int second) {
+  if constexpr (BITS == 8) return 32 * grp + 8 * j + 2 * p + second;
+  if constexpr (BITS == 4) return 32 * grp + 8 * j + p + 4 * second;
+  return 32 * grp + 16 * (j >> 1) + 4 * (j & 1) + p + 8 * second;
 }
 
 // Geometry of one 32-token tile as staged in LDS:
@@ -134,7 +164,7 @@ struct Geom {
   static constexpr int kMetaLanes = (kVm + kKm + kSp) / 16;
   static constexpr int kBytes = kK + kV + kVm + kKm + kSp;
   static constexpr int kLoads = kK / 1024 + kV / 1024 + 1;   // DMA instructions per tile
-  // the key-product B operand and subtrahends (channel axis only)
+  // the key-product B operand and zero-point operand (channel axis only)
   static constexpr int kWaveLds = KAXIS ? (4 * (2 * G + 1) * 4 * 16 + 4 * 4 * 4 * 4) : 0;
   // tile slots per wavefront: as many as fit the per-wavefront LDS budget
   // (kWaveBudget, chosen so that several 4-wavefront workgroups share a CU's
@@ -149,10 +179,18 @@ struct Geom {
 // (gfx950 global_load_lds_dwordx4). Issued from inline assembly so that the
 // compiler neither waits on it at every LDS read nor keeps stale LDS values
 // across it; completion is awaited explicitly with wait_vm().
+// dma16: per-lane 64-bit address. dma16s: wave-uniform base in SGPRs plus a
+// per-lane 32-bit byte offset.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(lds_base)
                : "memory", "m0");
 }
 template <int N>
@@ -162,8 +200,8 @@ __device__ __forceinline__ void wait_vm() {
 
 // LDS per wavefront for channel-axis keys: the B operand of the key product
 // for the current block (hi rows 0..G-1, lo rows G..2G-1, an all-zero row 2G;
-// [grp][row][chunk] fragments) and the per-channel subtrahends of the A
-// operand ([grp][chunk][pair]).
+// [grp][row][chunk] fragments) and the zero-point A operand, -z' in code-step units per
+// channel ([grp][chunk][pair]).
 template <int G>
 struct WaveLds {
   Frag qb[4][2 * G + 1][4];
@@ -193,10 +231,17 @@ __device__ __forceinline__ float grp_sum(float v) {
 // no rescaling; weights stay <= 2^kLazy.
 constexpr float kLazy = 8.f;
 
+// The value-scale factor 2^kv, kv = kKvTop - E, is set from the largest fp16
+// biased exponent E among the value scales seen so far, so that s * 2^kv < 2^6
+// and the P operand p * s * 2^kv < 2^14 stays inside fp16.
+constexpr int kKvTop = 20;
+
 // Token (0..31 within the tile) of A row m in MFMA row block e: row block e
 // holds tokens 8*(m/4) + 4e + m%4, so the output lane group g ends up with
 // the 8 consecutive tokens 8g..8g+7, the k-slots of its P operand.
 __device__ __forceinline__ int a_token(int e, int m) { return 8 * (m >> 2) + 4 * e + (m & 3); }
+
+__device__ __forceinline__ uint16_t umax16(uint16_t a, uint16_t b) { return a > b ? a : b; }
 
 template <int KB, int VB, int KAXIS, int G, bool SPARSE>
 __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, const uint16_t* __restrict__ q,
@@ -205,9 +250,12 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   constexpr int NB = Gm::kSlots;
   constexpr int kQMinK = -(1 << (KB - 1));
   constexpr int kQMinV = -(1 << (VB - 1));
-  constexpr bool kPermK = KB != 8;  // k-slot pairs (i, i+4) for 4/2-bit keys
-  constexpr bool kPermV = VB != 8;
+  constexpr bool kPermV = VB != 8;  // k-slot pairs (i, i+4) for 4/2-bit values
   static_assert(2 * G <= 16, "hi/lo rows must fit 16");
+  // value of one code step in the key / value operands, and its inverse
+  constexpr int kShK = code_shift<KB>(), kShV = code_shift<VB>();
+  const float kUnitK = __builtin_bit_cast(float, (uint32_t)(127 - 24 + kShK) << 23);
+  const float kInvUnitK = __builtin_bit_cast(float, (uint32_t)(127 + 24 - kShK) << 23);
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -236,19 +284,15 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   // query heads of this KV head, pre-scaled by softmax_scale * log2(e)
   const float qscale = p.scale * kLog2e;
   const uint16_t* qg = q + ((size_t)b * p.Hq + (size_t)h * G) * kD;
-  if constexpr (SPARSE) {
-    for (int i = tid; i < G * kD; i += 256) qsh[i / kD][i % kD] = h2f(qg[i]) * qscale;
+  if constexpr (SPARSE) {  // sparse entries add q * x directly to the scaled score
+    for (int i = tid; i < G * kD; i += 256) qsh[i / kD][i % kD] = h2f(qg[i]) * (qscale * kUnitK);
     __syncthreads();
   }
 
-  // channel axis: this lane builds the scaled query of 2 channels, all heads
-  // (slot pair p of octet q: channels (p, p+4) for 4/2-bit keys, (2p, 2p+1) for 8-bit)
-  int bc0 = 0, bc1 = 0;
-  {
-    const int oq = lane >> 2, op = lane & 3;
-    bc0 = kPermK ? 8 * oq + op : 8 * oq + 2 * op;
-    bc1 = kPermK ? bc0 + 4 : bc0 + 1;
-  }
+  // Channel axis: this lane builds the scaled query of 2 channels, all heads:
+  // k-slot pair bp of chunk bj in lane group bg, bq = lane / 4 = 4 bg + bj.
+  const int bq = lane >> 2, bp = lane & 3, bg = bq >> 2, bj = bq & 3;
+  const int bc0 = key_channel<KB>(bg, bj, bp, 0), bc1 = key_channel<KB>(bg, bj, bp, 1);
   float qv0[G], qv1[G];
   // token axis: the B operand is the raw fp16 query (exact), column n = head n mod G
   Frag qfrag[KAXIS ? 1 : 4];
@@ -269,9 +313,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
       for (int pp = 0; pp < 4; ++pp) {
         uint32_t v = 0;
         if (live) {
-          const int base = 32 * grp + 8 * j;
-          const int ch0 = kPermK ? base + pp : base + 2 * pp;
-          const int ch1 = kPermK ? ch0 + 4 : ch0 + 1;
+          const int ch0 = key_channel<KB>(grp, j, pp, 0), ch1 = key_channel<KB>(grp, j, pp, 1);
           v = (uint32_t)qg[hq * kD + ch0] | ((uint32_t)qg[hq * kD + ch1] << 16);
         }
         qfrag[j].p[pp] = v;
@@ -284,127 +326,140 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   const int tq = (Q > ts0) ? min((Q - ts0 + kBlock - 1) / kBlock, ntiles) : 0;  // quantized tiles
   const int nw = (w < tq) ? (tq - w + 3) / 4 : 0;                               // of them, mine
 
-  // DMA of quantized tile i of this wavefront into slot `slot`.
-  auto issue = [&](int i, int slot) {
-    const int t0 = ts0 + (w + 4 * i) * kBlock;
+  // DMA sources of the next tile to issue. Key codes and value blocks: a
+  // wave-uniform base plus lane * 16 (+ 1 KiB steps); metadata: the lanes
+  // gather 16-byte pieces of three arrays through per-lane pointers. Each
+  // advances by 4 tiles per issue (the wavefront takes every 4th tile).
+  const int tw0 = ts0 + w * kBlock;
+  const uint8_t* kgs = c.k_codes + (bh * c.T + tw0) * (size_t)Gm::kRowK;
+  const uint8_t* vgs = c.v_codes + (bh * (c.T / kBlock) + tw0 / kBlock) * (size_t)Gm::kV;
+  const uint8_t* mgp;
+  uint32_t mstep;
+  if (lane < 8) {
+    mgp = reinterpret_cast<const uint8_t*>(c.v_meta + bh * c.T + tw0) + lane * 16;
+    mstep = 4 * kBlock * 4;
+  } else if (lane < 8 + Gm::kKm / 16) {
+    const uint32_t* km = KAXIS ? c.k_meta + (bh * (c.T / kBlock) + tw0 / kBlock) * kD
+                               : c.k_meta + bh * c.T + tw0;
+    mgp = reinterpret_cast<const uint8_t*>(km) + (lane - 8) * 16;
+    mstep = KAXIS ? 4 * kD * 4 : 4 * kBlock * 4;
+  } else {
+    const int sl = min(lane - 8 - Gm::kKm / 16, 15);
+    mgp = reinterpret_cast<const uint8_t*>(c.k_sparse + (bh * c.T + tw0) * 2) + sl * 16;
+    mstep = 4 * kBlock * 8;
+  }
+  const uint32_t loff = lane * 16;
+
+  // DMA of the next tile of this wavefront into slot `slot`.
+  auto issue = [&](int slot) {
     const uint32_t lb = wbase_lds + slot * Gm::kBytes;
-    const uint8_t* kg = c.k_codes + (bh * c.T + t0) * (size_t)Gm::kRowK + lane * 16;
 #pragma unroll
-    for (int x = 0; x < Gm::kK / 1024; ++x) dma16(kg + x * 1024, lb + x * 1024);
-    const uint8_t* vg = c.v_codes + (bh * (c.T / kBlock) + t0 / kBlock) * (size_t)Gm::kV + lane * 16;
+    for (int x = 0; x < Gm::kK / 1024; ++x) dma16s(kgs, loff + x * 1024, lb + x * 1024);
 #pragma unroll
-    for (int x = 0; x < Gm::kV / 1024; ++x) dma16(vg + x * 1024, lb + Gm::kK + x * 1024);
-    if (lane < Gm::kMetaLanes) {
-      const uint8_t* mg;
-      if (lane < 8) {
-        mg = reinterpret_cast<const uint8_t*>(c.v_meta + bh * c.T + t0) + lane * 16;
-      } else if (lane < 8 + Gm::kKm / 16) {
-        const uint32_t* km = KAXIS ? c.k_meta + (bh * (c.T / kBlock) + t0 / kBlock) * kD
-                                   : c.k_meta + bh * c.T + t0;
-        mg = reinterpret_cast<const uint8_t*>(km) + (lane - 8) * 16;
-      } else {
-        mg = reinterpret_cast<const uint8_t*>(c.k_sparse + (bh * c.T + t0) * 2) +
-             (lane - 8 - Gm::kKm / 16) * 16;
-      }
-      dma16(mg, lb + Gm::kK + Gm::kV);
-    }
+    for (int x = 0; x < Gm::kV / 1024; ++x) dma16s(vgs, loff + x * 1024, lb + Gm::kK + x * 1024);
+    if (lane < Gm::kMetaLanes) dma16(mgp, lb + Gm::kK + Gm::kV);
+    kgs += 4 * Gm::kK;
+    vgs += 4 * Gm::kV;
+    mgp += mstep;
   };
 
-  const h2v vofs2 = {(_Float16)(1024 - kQMinV), (_Float16)(1024 - kQMinV)};
-  const h2v kofs2 = {(_Float16)(1024 - kQMinK), (_Float16)(1024 - kQMinK)};
-  const uint32_t kmask = vconst(KB == 2 ? 0x00030003u : 0x000F000Fu);
-  const uint32_t vmask = vconst(VB == 2 ? 0x00030003u : 0x000F000Fu);
-  const uint32_t kmagic = vconst(kMagic1024);
-
-  // row factors of the P operand: hi rows (c16 < G) keep p*s, lo rows take the
-  // residual p*s - rtz16(p*s), rows >= 2G are zero
-  const float rowkeep = live ? 1.f : 0.f;
-  const float rowlo = (c16 >= G && live) ? 1.f : 0.f;
-
   float m_ref = -INFINITY, l_run = 0.f;
-  f4v acc[8];
+  int vE = 0;                       // exponent the value-scale factor is set for
+  f4v acc[8], accz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
+  const float rowlo = (c16 >= G && c16 < 2 * G) ? 1.f : 0.f;  // lo rows of P
+  // zero-point operands: (z - qmin) in code-step units, from the fp16 z
+  constexpr _Float16 kZk = (_Float16)((float)(1 << kShK) * kTwoM24);
+  constexpr _Float16 kZkOfs = (_Float16)(kQMinK * (float)(1 << kShK) * kTwoM24);
+  constexpr _Float16 kZv = (_Float16)((float)(1 << kShV) * kTwoM24);
+  constexpr _Float16 kZvOfs = (_Float16)(-kQMinV * (float)(1 << kShV) * kTwoM24);
 
   // ---- scores of one tile -> online softmax -> P.V ---------------------------
-  // sc[4e + r] is the score of token 8grp + 4e + r (log2 units); vm[i] the value
-  // meta of token 8grp + i; vcode(j) gives the lane's value codes of chunk j.
-  auto softmax_pv = [&](float (&sc)[8], const uint32_t (&vm)[8], const uint32_t (&vcl)[8],
+  // sc[4e + r] is the scaled score (score = sc * cs + const) of token
+  // 8grp + 4e + r; vm[i] the value meta of token 8grp + i; vcl/vch[j] the
+  // lane's value codes of channel chunk j.
+  auto softmax_pv = [&](float (&sc)[8], float cs, const uint32_t (&vm)[8], const uint32_t (&vcl)[8],
                         const uint32_t (&vch)[8], int t0) {
     const int nvalid = ts1 - t0;
-    float mx = -INFINITY;
+    if (nvalid < kBlock) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (8 * grp + 4 * (i >> 2) + (i & 3) >= nvalid) sc[i] = -INFINITY;
-      mx = fmaxf(mx, sc[i]);
+      for (int i = 0; i < 8; ++i)
+        if (8 * grp + i >= nvalid) sc[i] = -INFINITY;
     }
-    if (__builtin_amdgcn_ballot_w64(live && mx > m_ref + kLazy)) {
-      const float m_new = fmaxf(m_ref, grp_max(mx));
+    const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    if (__builtin_amdgcn_ballot_w64(live && __builtin_fmaf(mx, cs, -m_ref) > kLazy)) {
+      const float m_new = fmaxf(m_ref, grp_max(mx * cs));
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
       float ar[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, (4 * grp + r) & (G - 1), 64);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int r = 0; r < 4; ++r) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[j][r] *= ar[r];
+        for (int j = 0; j < 8; ++j) acc[j][r] *= ar[r];
+        accz[r] *= ar[r];
+      }
       l_run *= alpha;
       m_ref = m_new;
     }
-    // Magic exponent vx of this lane group's value operand: the largest of its
-    // 8 value scales is brought to [1, 2) in P = p * s * 2^-vx, and the value
-    // codes carry the 2^vx back (B = (u - z') * 2^vx), so the product is
-    // unchanged; k-slots of one lane group meet only each other in the MFMA.
-    float sv[8];
+    // value-scale exponent: raise it when a scale of this tile reaches 2^6 * 2^-kv
+    const uint16_t smax =
+        umax16(umax16(umax16((uint16_t)vm[0], (uint16_t)vm[1]), umax16((uint16_t)vm[2], (uint16_t)vm[3])),
+               umax16(umax16((uint16_t)vm[4], (uint16_t)vm[5]), umax16((uint16_t)vm[6], (uint16_t)vm[7])));
+    if (__builtin_amdgcn_ballot_w64(smax >= (uint16_t)((vE + 1) << 10))) {
+      uint32_t sm = smax;
+      sm = max(sm, (uint32_t)__shfl_xor((int)sm, 16, 64));
+      sm = max(sm, (uint32_t)__shfl_xor((int)sm, 32, 64));
+      const int e_new = max(vE, (int)__builtin_amdgcn_readfirstlane(sm >> 10));
+      const float f = __builtin_bit_cast(float, (uint32_t)(127 + vE - e_new) << 23);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sv[i] = h2f((uint16_t)(vm[i] & 0xFFFFu));
-    const float smax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                             fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    const int ex = (smax > 0.f) ? (int)((__builtin_bit_cast(uint32_t, smax) >> 23) & 0xFF) - 127 : 0;
-    const int vx = min(max(ex, -24), 5);
-    const uint32_t vmagic1 = (uint32_t)(25 + vx) << 10;
-    const uint32_t vmagic = vmagic1 * 0x10001u;
-    const uint32_t vmagic_b = (vmagic1 >> 8) * 0x01010101u;
-    const float vpow = __builtin_ldexpf(rowkeep, -vx);
-    const uint32_t p2 = (vx >= -14) ? (uint32_t)(vx + 15) << 10 : 1u << (vx + 24);  // fp16 2^vx
-    const h2v vpow2 = as_h2(p2 * 0x10001u);
-    float pv[8];
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j][r] *= f;
+        accz[r] *= f;
+      }
+      l_run *= f;
+      vE = e_new;
+    }
+    const float kvm = (float)(kKvTop - vE) - m_ref;
+    // P = p * s * 2^kv; lo rows keep p * s * 2^kv - fp16(p * s * 2^kv)
+    float a[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float pr = __builtin_amdgcn_exp2f(sc[i] - m_ref);
-      l_run += pr;
-      const float x = pr * (sv[i] * vpow);
-      pv[i] = x - rowlo * trunc16(x);
+      const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cs, kvm));
+      l_run += x;
+      a[i] = mul_lo(x, vm[i]);
     }
-    Frag pf;
-    uint32_t vsub[4];
+    Frag pf, bz;
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
       const int i0 = kPermV ? pp : 2 * pp;
       const int i1 = kPermV ? pp + 4 : 2 * pp + 1;
-      pf.p[pp] = pk_rtz(pv[i0], pv[i1]);
-      const uint32_t zz = perm(vm[i1], vm[i0], 0x07060302u);  // (z_i0, z_i1)
-      vsub[pp] = as_u32((as_h2(zz) + vofs2) * vpow2);
+      const uint32_t hi = pk_rtz(a[i0], a[i1]);
+      pf.p[pp] = pk_rtz(__builtin_fmaf(f16lo(hi), -rowlo, a[i0]), __builtin_fmaf(f16hi(hi), -rowlo, a[i1]));
+      // (z'_i0, z'_i1) in code-step units, z' = z - qmin
+      bz.p[pp] = pk_fma16(perm(vm[i1], vm[i0], 0x07060302u), kZv, kZvOfs);
     }
+    accz = mfma(pf, bz, accz);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const Frag vf = unpack8<VB>(vcl[j], vch[j], 0, vmask, vmagic, vmagic_b, vsub);
-      acc[j] = mfma(pf, vf, acc[j]);
-    }
+    for (int j = 0; j < 8; ++j) acc[j] = mfma(pf, codes8<VB>(vcl[j], vch[j], 1), acc[j]);
   };
 
   // the B operand of the key product for a block: scaled query (hi/lo) with
-  // per-channel scales s0, s1 of this lane's two build channels
-  auto build_qb = [&](float s0, float s1, uint32_t km0, uint32_t km1, bool with_zero) {
-    const int bq = lane >> 2, bp = lane & 3, bg = bq >> 2, bj = bq & 3;
+  // the per-channel scales in the low halves of km0, km1; with_zero also
+  // writes the zero-point operand -(z - qmin) (code-step units) from their high halves
+  auto build_qb = [&](uint32_t km0, uint32_t km1, bool with_zero) {
     wave_lds_fence();
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float v0 = qv0[hh] * s0, v1 = qv1[hh] * s1;
-      wl.qb[bg][hh][bj].p[bp] = pk_rtz(v0, v1);
-      wl.qb[bg][G + hh][bj].p[bp] = pk_rtz(v0 - trunc16(v0), v1 - trunc16(v1));
+      const float v0 = mul_lo(qv0[hh], km0), v1 = mul_lo(qv1[hh], km1);
+      const uint32_t hi = pk_rtz(v0, v1);
+      wl.qb[bg][hh][bj].p[bp] = hi;
+      wl.qb[bg][G + hh][bj].p[bp] = pk_rtz(__builtin_fmaf(f16lo(hi), -1.f, v0), __builtin_fmaf(f16hi(hi), -1.f, v1));
     }
-    if (with_zero) wl.zc[bg][bj][bp] = as_u32(as_h2(perm(km1, km0, 0x07060302u)) + kofs2);
+    if (with_zero) wl.zc[bg][bj][bp] = pk_fma16(perm(km1, km0, 0x07060302u), -kZk, kZkOfs);
     wave_lds_fence();
   };
 
@@ -412,10 +467,10 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   if (nw > 0) {
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i)
-      if (i < nw) issue(i, i);
+      if (i < nw) issue(i);
     for (int i = 0; i < nw; ++i) {
       const int slot = i % NB;
-      if (i + NB - 1 < nw) issue(i + NB - 1, (i + NB - 1) % NB);
+      if (i + NB - 1 < nw) issue((i + NB - 1) % NB);
       // tile i has landed once at most (tiles issued after it) x loads remain
       switch (min(NB - 1, nw - 1 - i)) {
         case 0: wait_vm<0>(); break;
@@ -450,24 +505,31 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           kc[e][x + 1] = y.y;
         }
       }
+      auto key_frag = [&](int e, int j) -> Frag {
+        if constexpr (KB == 4) return codes8<4>(kc[e][j], 0u, 0);
+        else if constexpr (KB == 8) return codes8<8>(kc[e][2 * j], kc[e][2 * j + 1], 0);
+        else return codes8<2>(kc[e][j >> 1], 0u, j & 1);
+      };
       float sc[8];
-      f4v s[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
+      float cs;
       if constexpr (KAXIS) {
-        const uint32_t km0 = kmeta[bc0], km1 = kmeta[bc1];
-        build_qb(h2f((uint16_t)(km0 & 0xFFFFu)), h2f((uint16_t)(km1 & 0xFFFFu)), km0, km1, true);
+        build_qb(kmeta[bc0], kmeta[bc1], true);
+        // zero-point term, the same for every token of the block
+        f4v cz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const Frag az = *reinterpret_cast<const Frag*>(wl.zc[grp][j]);
+          cz = mfma(az, wl.qb[grp][brow_hi][j], cz);
+          cz = mfma(az, wl.qb[grp][brow_lo][j], cz);
+        }
+        f4v s[2] = {cz, cz};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const Frag qh = wl.qb[grp][brow_hi][j];
           const Frag ql = wl.qb[grp][brow_lo][j];
-          uint32_t zsub[4];
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp) zsub[pp] = wl.zc[grp][j][pp];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            Frag kf;
-            if constexpr (KB == 4) kf = unpack8<4>(kc[e][j], 0u, 0, kmask, kmagic, 0u, zsub);
-            else if constexpr (KB == 8) kf = unpack8<8>(kc[e][2 * j], kc[e][2 * j + 1], 0, kmask, kmagic, 0x64646464u, zsub);
-            else kf = unpack8<2>(kc[e][j >> 1], 0u, j & 1, kmask, kmagic, 0u, zsub);
+            const Frag kf = key_frag(e, j);
             s[e] = mfma(kf, qh, s[e]);
             s[e] = mfma(kf, ql, s[e]);
           }
@@ -476,6 +538,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
         for (int e = 0; e < 2; ++e)
 #pragma unroll
           for (int r = 0; r < 4; ++r) sc[4 * e + r] = s[e][r];
+        cs = kInvUnitK;
       } else {
         uint32_t km[8];
         {
@@ -484,33 +547,30 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           km[0] = a.x; km[1] = a.y; km[2] = a.z; km[3] = a.w;
           km[4] = bb.x; km[5] = bb.y; km[6] = bb.z; km[7] = bb.w;
         }
+        f4v s[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
+          // zero-point term of the row's token: -(z - qmin) * sum_c q_c
           const uint32_t ka = kmeta[a_token(e, c16)];
-          const uint32_t zt = (ka >> 16) | (ka & 0xFFFF0000u);  // (z, z)
-          const uint32_t zs = as_u32(as_h2(zt) + kofs2);
-          const uint32_t zsub[4] = {zs, zs, zs, zs};
+          const uint32_t az1 = pk_fma16(perm(ka, ka, 0x07060706u), -kZk, kZkOfs);
+          const Frag az = {{az1, az1, az1, az1}};
+          s[e] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            Frag kf;
-            if constexpr (KB == 4) kf = unpack8<4>(kc[e][j], 0u, 0, kmask, kmagic, 0u, zsub);
-            else if constexpr (KB == 8) kf = unpack8<8>(kc[e][2 * j], kc[e][2 * j + 1], 0, kmask, kmagic, 0x64646464u, zsub);
-            else kf = unpack8<2>(kc[e][j >> 1], 0u, j & 1, kmask, kmagic, 0u, zsub);
-            s[e] = mfma(kf, qfrag[j], s[e]);
-          }
+          for (int j = 0; j < 4; ++j) s[e] = mfma(az, qfrag[j], s[e]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s[e] = mfma(key_frag(e, j), qfrag[j], s[e]);
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            sc[4 * e + r] = s[e][r] * (h2f((uint16_t)(km[4 * e + r] & 0xFFFFu)) * qscale);
+          for (int r = 0; r < 4; ++r) sc[4 * e + r] = mul_lo(s[e][r], km[4 * e + r]);
+        cs = kInvUnitK * qscale;
       }
       if constexpr (SPARSE) {
 #pragma unroll
         for (int i2 = 0; i2 < 8; ++i2) {
           const uint2 rec = reinterpret_cast<const uint2*>(spr)[8 * grp + i2];
-          sc[i2] += qsh[hq][rec.y & 0xFFFFu] * h2f((uint16_t)(rec.x & 0xFFFFu)) +
-                    qsh[hq][rec.y >> 16] * h2f((uint16_t)(rec.x >> 16));
+          sc[i2] += qsh[hq][rec.y & 0xFFFFu] * f16lo(rec.x) + qsh[hq][rec.y >> 16] * f16hi(rec.x);
         }
       }
       // value codes: channel 16j + c16, tokens 8grp .. 8grp+7 of the block
@@ -526,11 +586,12 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           vcl[j] = x.x;
           vch[j] = x.y;
         } else {
-          vcl[j] = reinterpret_cast<const uint16_t*>(rec)[grp];
+          // 8 two-bit fields -> byte 1 (tokens 0..3) and byte 3 (tokens 4..7)
+          vcl[j] = perm(0u, reinterpret_cast<const uint16_t*>(rec)[grp], 0x010C000Cu);
           vch[j] = 0u;
         }
       }
-      softmax_pv(sc, vm, vcl, vch, t0);
+      softmax_pv(sc, cs, vm, vcl, vch, t0);
     }
   }
 
@@ -548,33 +609,41 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           else if constexpr (VB == 8) {
             const uint2 x = reinterpret_cast<const uint2*>(rec)[grp];
             vcl[j] = x.x; vch[j] = x.y;
-          } else { vcl[j] = reinterpret_cast<const uint16_t*>(rec)[grp]; vch[j] = 0u; }
+          } else {
+            vcl[j] = perm(0u, reinterpret_cast<const uint16_t*>(rec)[grp], 0x010C000Cu);
+            vch[j] = 0u;
+          }
         }
         const uint4* vmg = reinterpret_cast<const uint4*>(c.v_meta + bh * c.T + t0 + 8 * grp);
         const uint4 a = vmg[0], bb = vmg[1];
         vm[0] = a.x; vm[1] = a.y; vm[2] = a.z; vm[3] = a.w;
         vm[4] = bb.x; vm[5] = bb.y; vm[6] = bb.z; vm[7] = bb.w;
       }
-      // B operand: query scaled by the softmax factor only, hi/lo
-      build_qb(1.f, 1.f, 0u, 0u, false);
+      // B operand: query scaled by the softmax factor only (scale 1.0), hi/lo
+      build_qb(0x3C00u, 0x3C00u, false);
       f4v s[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int tt = t0 + a_token(e, c16);
         const bool ok = tt < ts1;
-        const uint16_t* kr = c.k_resid + (bh * c.R + (ok ? tt - Q : 0)) * kD + 32 * grp;
+        // the lane group's 32 fp16 keys, channels 32grp .. 32grp+31
+        const uint4* kr = reinterpret_cast<const uint4*>(c.k_resid + (bh * c.R + (ok ? tt - Q : 0)) * kD + 32 * grp);
+        uint32_t rw[16];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          uint4 v = kr[x];
+          if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
+          rw[4 * x] = v.x; rw[4 * x + 1] = v.y; rw[4 * x + 2] = v.z; rw[4 * x + 3] = v.w;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          uint4 x = reinterpret_cast<const uint4*>(kr + 8 * j)[0];
-          if (!ok) x = make_uint4(0, 0, 0, 0);
+          // k-slot pair pp of chunk j: the keys of the channels the codes use
           Frag kf;
-          if (kPermK) {  // pairs (channel p, p+4)
-            kf.p[0] = perm(x.z, x.x, 0x05040100u);
-            kf.p[1] = perm(x.z, x.x, 0x07060302u);
-            kf.p[2] = perm(x.w, x.y, 0x05040100u);
-            kf.p[3] = perm(x.w, x.y, 0x07060302u);
-          } else {
-            kf.p[0] = x.x; kf.p[1] = x.y; kf.p[2] = x.z; kf.p[3] = x.w;
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            const int c0 = key_channel<KB>(0, j, pp, 0), c1 = key_channel<KB>(0, j, pp, 1);
+            const uint32_t sel = ((c0 & 1) ? 0x0302u : 0x0100u) | ((c1 & 1) ? 0x07060000u : 0x05040000u);
+            kf.p[pp] = perm(rw[c1 >> 1], rw[c0 >> 1], sel);
           }
           s[e] = mfma(kf, wl.qb[grp][brow_hi][j], s[e]);
           s[e] = mfma(kf, wl.qb[grp][brow_lo][j], s[e]);
@@ -584,13 +653,16 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
 #pragma unroll
       for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[4 * e + r] = s[e][r];
-      softmax_pv(sc, vm, vcl, vch, t0);
+        for (int r = 0; r < 4; ++r) sc[4 * e + r] = s[e][r] * kUnitK;
+      softmax_pv(sc, kInvUnitK, vm, vcl, vch, t0);
     }
   }
 
   // ---- merge the wavefronts of the workgroup --------------------------------
-  const float lsum = grp_sum(l_run);
+  // o = (acc - accz) / (value code step) * 2^-kv, l = l_run * 2^-kv
+  const float ofac = __builtin_bit_cast(float, (uint32_t)(127 + 24 - kShV - kKvTop + vE) << 23);
+  const float lfac = __builtin_bit_cast(float, (uint32_t)(127 - kKvTop + vE) << 23);
+  const float lsum = grp_sum(l_run) * lfac;
   __syncthreads();  // every wavefront is done with its slots
   MergeLds<G>& mg = *reinterpret_cast<MergeLds<G>*>(smem);
   if (grp == 0 && c16 < G) {
@@ -602,7 +674,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * grp + r;
-      if (row < 2 * G) mg.o[w][row][16 * j + c16] = acc[j][r];
+      if (row < 2 * G) mg.o[w][row][16 * j + c16] = (acc[j][r] - accz[r]) * ofac;
     }
   __syncthreads();
   const bool single = nsplit_b <= 1;
