@@ -1,10 +1,14 @@
 // C-ABI entry points of the kvq library: argument validation on the host,
 // then kernel launches on the caller's stream. No allocation, no
-// synchronization (except under KVQ_DEBUG=1), no state kept between calls.
+// synchronization (except under KVQ_DEBUG=1, which also prints HIP errors),
+// no state kept between calls beyond per-device constants read once (compute
+// units, resident attention workgroups per compute unit).
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "kvq.h"
 #include "kvq_internal.h"
@@ -21,11 +25,16 @@ bool debug_sync() {
   return on != 0;
 }
 
+kvq_status hip_failed(hipError_t e, const char* where) {
+  if (debug_sync()) fprintf(stderr, "kvq: %s: %s\n", where, hipGetErrorString(e));
+  return KVQ_EHIP;
+}
+
 kvq_status after_launch(hipError_t e, hipStream_t st) {
-  if (e != hipSuccess) return KVQ_EHIP;
+  if (e != hipSuccess) return hip_failed(e, "launch");
   if (debug_sync()) {
-    if (hipStreamSynchronize(st) != hipSuccess) return KVQ_EHIP;
-    if (hipGetLastError() != hipSuccess) return KVQ_EHIP;
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_failed(e, "stream synchronize");
+    if ((e = hipGetLastError()) != hipSuccess) return hip_failed(e, "after synchronize");
   }
   return KVQ_OK;
 }
@@ -45,6 +54,45 @@ int compute_units() {
     cache[dev] = n;
   }
   return cache[dev];
+}
+
+// Split plan: 32-token tiles per split. Each (sequence, KV head) is cut into
+// splits of `tps` tiles, one workgroup each; `slots` workgroups run at once.
+// The makespan is estimated as whole rounds of slots, each as long as one
+// full split plus a fixed per-workgroup overhead (first-tile latency, merge),
+// and the split length with the smallest estimate wins (ties: the longer).
+// Splits are at least kMinSplitTiles long, which bounds their number by the
+// workspace size.
+int plan_tiles_per_split(const kvq_cache* cache, int n_kv_heads, int64_t slots) {
+  constexpr int kOverheadTiles = 4;
+  int max_tiles = 0;
+  for (int b = 0; b < cache->batch; ++b)
+    max_tiles = std::max(max_tiles, (int)((cache->len_host[b] + kBlock - 1) / kBlock));
+  if (max_tiles <= kMinSplitTiles) return std::max(max_tiles, 1);
+  int best_tps = max_tiles, prev = -1;
+  double best = 1e300;
+  for (int ns = 1;; ++ns) {
+    const int tps = (max_tiles + ns - 1) / ns;
+    if (tps < kMinSplitTiles) break;
+    if (tps == prev) continue;
+    prev = tps;
+    int64_t wgs = 0, work = 0;
+    for (int b = 0; b < cache->batch; ++b) {
+      const int t = (int)((cache->len_host[b] + kBlock - 1) / kBlock);
+      wgs += std::max(1, (t + tps - 1) / tps);
+      work += t;
+    }
+    wgs *= n_kv_heads;
+    work *= n_kv_heads;
+    const double wg_time = tps + kOverheadTiles;
+    const double rounds = std::ceil((double)(work + wgs * kOverheadTiles) / ((double)slots * wg_time));
+    const double cost = std::max(rounds, 1.0) * wg_time;
+    if (cost < best) {
+      best = cost;
+      best_tps = tps;
+    }
+  }
+  return best_tps;
 }
 
 kvq_status check_config(const kvq_config* cfg) {
@@ -203,26 +251,17 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   if ((s = check_cache(cfg, cache)) != KVQ_OK) return s;
   if (!q || !out || !ws || !aligned(q) || !aligned(out) || !aligned(ws)) return KVQ_EINVAL;
   if (ws_bytes < kvq_workspace_bytes(cfg, cache->batch, cache->max_tokens)) return KVQ_EWORKSPACE;
-  int lmax = 0;
-  int64_t total = 0;
-  for (int b = 0; b < cache->batch; ++b) {
-    lmax = std::max(lmax, (int)cache->len_host[b]);
-    total += cache->len_host[b];
-  }
+  const CacheView v = view_of(cfg, cache);
   AttnPlan p;
   p.Hq = cfg->n_q_heads;
   p.group = cfg->n_q_heads / cfg->n_kv_heads;
   p.scale = softmax_scale;
-  // tokens per split: about two workgroups per compute unit over all
-  // (sequence, KV head) pairs, each at least 256 and at most 2048 tokens
-  // (bounds the imbalance of ragged lengths), a multiple of 32
-  const int64_t target = 2 * (int64_t)compute_units();
-  int64_t per = (total * cfg->n_kv_heads + target - 1) / target;
-  per = std::min<int64_t>(std::max<int64_t>(per, kMinSplitTokens), 2048);
-  per = (per + kBlock - 1) / kBlock * kBlock;
-  p.tokens_per_split = (int)per;
-  p.n_split = std::max(1, (int)((lmax + per - 1) / per));
-  const CacheView v = view_of(cfg, cache);
+  const int tps = plan_tiles_per_split(cache, cfg->n_kv_heads,
+                                       compute_units() * attention_blocks_per_cu(v, p.group));
+  int lmax = 0;
+  for (int b = 0; b < cache->batch; ++b) lmax = std::max(lmax, (int)cache->len_host[b]);
+  p.tokens_per_split = tps * kBlock;
+  p.n_split = std::max(1, (lmax + p.tokens_per_split - 1) / p.tokens_per_split);
   hipStream_t st = (hipStream_t)stream;
   return after_launch(launch_decode_attention(v, p, (const uint16_t*)q, out, (float*)ws, st), st);
 }

@@ -44,6 +44,8 @@
 // merges with a log-sum-exp. (Merging in the last-arriving workgroup instead
 // needs device-scope fences, whose L2 writeback and invalidation cost far more
 // than the extra launch on this chip.)
+#include <algorithm>
+
 #include "kvq_device.h"
 
 namespace kvq {
@@ -726,9 +728,31 @@ __global__ __launch_bounds__(128) void combine_kernel(CacheView c, AttnPlan p, c
   out[(size_t)bq * kD + ch] = (l > 0.f) ? o / l : 0.f;
 }
 
+// Launch of one kernel variant, or (occ != nullptr) its resident workgroups
+// per compute unit.
 template <int KB, int VB, int KAXIS, int G, bool SPARSE>
 hipError_t launch_t(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
-                    hipStream_t st) {
+                    hipStream_t st, int* occ) {
+  if (occ) {
+    const void* fn = reinterpret_cast<const void*>(attn_kernel<KB, VB, KAXIS, G, SPARSE>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, attn_kernel<KB, VB, KAXIS, G, SPARSE>, 256, 0) ==
+            hipSuccess && *occ > 0)
+      return hipSuccess;
+    (void)hipGetLastError();  // the query is optional: do not leave its error behind
+    // estimate from the kernel's resources: one wavefront per SIMD per
+    // workgroup, 512 VGPRs per SIMD lane, 160 KiB of LDS per compute unit
+    hipFuncAttributes a;
+    if (hipFuncGetAttributes(&a, fn) != hipSuccess) {
+      (void)hipGetLastError();
+      *occ = 1;
+      return hipSuccess;
+    }
+    const int vgprs = a.numRegs > 0 ? (a.numRegs + 7) / 8 * 8 : 512;
+    const int by_vgpr = 512 / vgprs;
+    const int by_lds = a.sharedSizeBytes > 0 ? (int)((160 * 1024) / a.sharedSizeBytes) : 8;
+    *occ = std::max(1, std::min(std::min(by_vgpr, by_lds), 8));
+    return hipSuccess;
+  }
   dim3 grid(p.n_split, c.H, c.B);
   hipLaunchKernelGGL((attn_kernel<KB, VB, KAXIS, G, SPARSE>), grid, dim3(256), 0, st, c, p, q, out, ws);
   return hipGetLastError();
@@ -736,31 +760,41 @@ hipError_t launch_t(const CacheView& c, const AttnPlan& p, const uint16_t* q, fl
 
 template <int KB, int VB, int KAXIS, bool SPARSE>
 hipError_t dispatch_g(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
-                      hipStream_t st) {
+                      hipStream_t st, int* occ) {
   switch (p.group) {
-    case 1: return launch_t<KB, VB, KAXIS, 1, SPARSE>(c, p, q, out, ws, st);
-    case 2: return launch_t<KB, VB, KAXIS, 2, SPARSE>(c, p, q, out, ws, st);
-    case 4: return launch_t<KB, VB, KAXIS, 4, SPARSE>(c, p, q, out, ws, st);
-    case 8: return launch_t<KB, VB, KAXIS, 8, SPARSE>(c, p, q, out, ws, st);
+    case 1: return launch_t<KB, VB, KAXIS, 1, SPARSE>(c, p, q, out, ws, st, occ);
+    case 2: return launch_t<KB, VB, KAXIS, 2, SPARSE>(c, p, q, out, ws, st, occ);
+    case 4: return launch_t<KB, VB, KAXIS, 4, SPARSE>(c, p, q, out, ws, st, occ);
+    case 8: return launch_t<KB, VB, KAXIS, 8, SPARSE>(c, p, q, out, ws, st, occ);
   }
   return hipErrorInvalidValue;
 }
 
 template <int KB, int VB>
 hipError_t dispatch_axis(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
-                         hipStream_t st) {
-  if (c.kaxis == 0) return dispatch_g<KB, VB, 0, false>(c, p, q, out, ws, st);
-  if (c.sparse) return dispatch_g<KB, VB, 1, true>(c, p, q, out, ws, st);
-  return dispatch_g<KB, VB, 1, false>(c, p, q, out, ws, st);
+                         hipStream_t st, int* occ) {
+  if (c.kaxis == 0) return dispatch_g<KB, VB, 0, false>(c, p, q, out, ws, st, occ);
+  if (c.sparse) return dispatch_g<KB, VB, 1, true>(c, p, q, out, ws, st, occ);
+  return dispatch_g<KB, VB, 1, false>(c, p, q, out, ws, st, occ);
 }
 
 template <int KB>
 hipError_t dispatch_vb(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
-                       hipStream_t st) {
+                       hipStream_t st, int* occ) {
   switch (c.vbits) {
-    case 8: return dispatch_axis<KB, 8>(c, p, q, out, ws, st);
-    case 4: return dispatch_axis<KB, 4>(c, p, q, out, ws, st);
-    case 2: return dispatch_axis<KB, 2>(c, p, q, out, ws, st);
+    case 8: return dispatch_axis<KB, 8>(c, p, q, out, ws, st, occ);
+    case 4: return dispatch_axis<KB, 4>(c, p, q, out, ws, st, occ);
+    case 2: return dispatch_axis<KB, 2>(c, p, q, out, ws, st, occ);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t dispatch(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
+                    hipStream_t st, int* occ) {
+  switch (c.kbits) {
+    case 8: return dispatch_vb<8>(c, p, q, out, ws, st, occ);
+    case 4: return dispatch_vb<4>(c, p, q, out, ws, st, occ);
+    case 2: return dispatch_vb<2>(c, p, q, out, ws, st, occ);
   }
   return hipErrorInvalidValue;
 }
@@ -769,16 +803,27 @@ hipError_t dispatch_vb(const CacheView& c, const AttnPlan& p, const uint16_t* q,
 
 hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out,
                                    float* ws, hipStream_t st) {
-  hipError_t e;
-  switch (c.kbits) {
-    case 8: e = dispatch_vb<8>(c, p, q, out, ws, st); break;
-    case 4: e = dispatch_vb<4>(c, p, q, out, ws, st); break;
-    case 2: e = dispatch_vb<2>(c, p, q, out, ws, st); break;
-    default: return hipErrorInvalidValue;
-  }
+  const hipError_t e = dispatch(c, p, q, out, ws, st, nullptr);
   if (e != hipSuccess || p.n_split <= 1) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(c.B * p.Hq), dim3(kD), 0, st, c, p, ws, out);
   return hipGetLastError();
+}
+
+int attention_blocks_per_cu(const CacheView& c, int group) {
+  // cached per device and kernel variant
+  static int cache[16][3][3][2][2][4];
+  const auto bi = [](int b) { return b == 2 ? 0 : (b == 4 ? 1 : 2); };
+  const int gi = group == 1 ? 0 : (group == 2 ? 1 : (group == 4 ? 2 : 3));
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = -1;
+  int* slot = dev >= 0 ? &cache[dev][bi(c.kbits)][bi(c.vbits)][c.kaxis ? 1 : 0][c.sparse ? 1 : 0][gi] : nullptr;
+  if (slot && *slot > 0) return *slot;
+  AttnPlan p{};
+  p.group = group;
+  int occ = 0;
+  if (dispatch(c, p, nullptr, nullptr, nullptr, nullptr, &occ) != hipSuccess || occ < 1) occ = 1;
+  if (slot) *slot = occ;
+  return occ;
 }
 
 }  // namespace kvq

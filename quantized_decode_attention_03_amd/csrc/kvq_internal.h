@@ -52,11 +52,15 @@ struct AttnPlan {
 hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p,
                                    const uint16_t* q, float* out, float* ws,
                                    hipStream_t st);
+// Workgroups of the attention kernel variant for (c, group) resident per
+// compute unit (at least 1).
+int attention_blocks_per_cu(const CacheView& c, int group);
 
 // Workspace: fp32 partials [B][Hq][n_split][kPartialFloats] = m, l, 2 pad,
 // o[128].
 constexpr int kPartialFloats = 4 + kD;
 constexpr int kMinSplitTokens = 256;
+constexpr int kMinSplitTiles = kMinSplitTokens / kBlock;
 // Upper bound on splits per (sequence, KV head) for a given capacity.
 inline int max_splits_for(int max_tokens) {
   return (max_tokens + kMinSplitTokens - 1) / kMinSplitTokens;
