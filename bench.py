@@ -237,7 +237,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"int{s.k_bits}/int{s.v_bits} codes, f32 math",
+        "dtype": f"f16 MFMA, f32 accumulate (int{s.k_bits}/int{s.v_bits} codes)",
         "data": "synthetic",
         "config": {"workload": s.name, "batch": s.batch, "n_q_heads": s.n_q_heads,
                    "n_kv_heads": s.n_kv_heads, "d_head": s.d_head, "seq_len": s.seq_len,
