@@ -27,12 +27,15 @@ Sources (by page title and section):
 Modules:
   quant   group quantize / dequantize, integer ranges, dense-and-sparse split
   cache   the cache state machine (append, residual flush), the documented
-          packed byte layout, dequantized tensors and float64 attention
+          packed byte layout, dequantized tensors, float64 attention, and the
+          log-sum-exp merge of split partials (softmax_partial, merge_partials)
   sizes   the bytes-per-token formula and the actual cache sizes
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against values the
 pages print, closed forms, invariants and brute force. One part has no pin in
 the pages: the bit layout of the packed bytes (``cache.pack``), which is this
 library's own documented format; its pin is the unpack/pack identity only
-("parity unpinned" by the pages).
+("parity unpinned" by the pages). The split merge is not on the pages either;
+it is pinned by its closed form (merged partials of any split equal the
+unsplit softmax result).
 """

@@ -268,3 +268,34 @@ def meta_words(s16, z16):
     """uint32 word per group: fp16 scale bits | fp16 zero bits << 16."""
     return (quant.f16_bits(s16).astype(np.uint32)
             | (quant.f16_bits(z16).astype(np.uint32) << 16))
+
+
+# ------------------------------------------------------- split-K merge
+def softmax_partial(sc, V):
+    """Softmax state of one token range (float64): m = the range's largest
+    score, l = sum exp(s - m), o = sum exp(s - m) * V_t. An empty range has
+    m = -inf, l = 0, o = 0. This is the state a split of the sequence hands to
+    the merge; the merge step is not on the pages (it is how a decode kernel
+    that splits a long sequence over several workgroups finishes), so it is
+    pinned only by its closed form: merging the partials of any split of the
+    tokens gives exactly the unsplit softmax result."""
+    sc = np.asarray(sc, np.float64)
+    V = np.asarray(V, np.float64)
+    if sc.size == 0:
+        return -np.inf, 0.0, np.zeros(V.shape[-1], np.float64)
+    m = float(sc.max())
+    p = np.exp(sc - m)
+    return m, float(p.sum()), p @ V
+
+
+def merge_partials(parts):
+    """Log-sum-exp merge of split partials: M = max m_i,
+    l = sum exp(m_i - M) l_i, o = sum exp(m_i - M) o_i, output o / l
+    (0 when every range is empty)."""
+    ms = [m for m, _, _ in parts]
+    M = max(ms)
+    if M == -np.inf:
+        return np.zeros_like(parts[0][2])
+    l = sum(np.exp(m - M) * li for m, li, _ in parts if m != -np.inf)
+    o = sum(np.exp(m - M) * oi for m, _, oi in parts if m != -np.inf)
+    return o / l

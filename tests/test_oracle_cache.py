@@ -251,3 +251,35 @@ def test_workload_generator_structure():
     s5 = W.spec(5)
     L = W.seq_lengths(s5)
     assert L.min() >= 1024 and L.max() <= 32768 and len(set(L.tolist())) > 100
+
+
+def test_split_merge_equals_unsplit():
+    # closed form of the split-K merge: any split of the tokens, merged with
+    # the log-sum-exp rule, reproduces the unsplit softmax result
+    from oracle.cache import softmax_partial, merge_partials
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        S = int(rng.integers(1, 300))
+        sc = rng.standard_normal(S) * rng.choice([0.5, 5.0, 60.0])
+        V = rng.standard_normal((S, 16))
+        p = np.exp(sc - sc.max())
+        want = (p @ V) / p.sum()
+        cuts = np.sort(rng.integers(0, S + 1, size=int(rng.integers(0, 6))))
+        bounds = [0] + cuts.tolist() + [S]
+        parts = [softmax_partial(sc[a:b], V[a:b]) for a, b in zip(bounds[:-1], bounds[1:])]
+        got = merge_partials(parts)
+        assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+
+
+def test_split_merge_degenerate_cases():
+    from oracle.cache import softmax_partial, merge_partials
+    V = np.arange(12, dtype=np.float64).reshape(3, 4)
+    empty = softmax_partial(np.zeros(0), np.zeros((0, 4)))
+    assert empty[0] == -np.inf and empty[1] == 0.0 and not np.any(empty[2])
+    # every range empty -> 0 (the empty-sequence convention)
+    assert not np.any(merge_partials([empty, empty]))
+    # one token per range: weights exp(s_t - max) / sum
+    sc = np.array([1.0, 3.0, 2.0])
+    parts = [softmax_partial(sc[i:i + 1], V[i:i + 1]) for i in range(3)] + [empty]
+    w = np.exp(sc - 3.0) / np.exp(sc - 3.0).sum()
+    assert np.allclose(merge_partials(parts), w @ V, rtol=0, atol=1e-13)
