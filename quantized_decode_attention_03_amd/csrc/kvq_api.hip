@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include "kvq.h"
@@ -44,16 +45,16 @@ bool bits_ok(int b) { return b == 2 || b == 4 || b == 8; }
 // Compute units of the current device (read once per device; 256 if the
 // query fails).
 int compute_units() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];  // 0 = not read yet; threads may race to fill it
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 // Split plan: 32-token tiles per split. Each (sequence, KV head) is cut into

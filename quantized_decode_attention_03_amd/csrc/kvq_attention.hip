@@ -45,6 +45,7 @@
 // needs device-scope fences, whose L2 writeback and invalidation cost far more
 // than the extra launch on this chip.)
 #include <algorithm>
+#include <atomic>
 
 #include "kvq_device.h"
 
@@ -810,19 +811,24 @@ hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p, const 
 }
 
 int attention_blocks_per_cu(const CacheView& c, int group) {
-  // cached per device and kernel variant
-  static int cache[16][3][3][2][2][4];
+  // cached per device and kernel variant (0 = not queried yet; threads may
+  // race to fill an entry with the same value)
+  static std::atomic<int> cache[16][3][3][2][2][4];
   const auto bi = [](int b) { return b == 2 ? 0 : (b == 4 ? 1 : 2); };
   const int gi = group == 1 ? 0 : (group == 2 ? 1 : (group == 4 ? 2 : 3));
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = -1;
-  int* slot = dev >= 0 ? &cache[dev][bi(c.kbits)][bi(c.vbits)][c.kaxis ? 1 : 0][c.sparse ? 1 : 0][gi] : nullptr;
-  if (slot && *slot > 0) return *slot;
+  std::atomic<int>* slot =
+      dev >= 0 ? &cache[dev][bi(c.kbits)][bi(c.vbits)][c.kaxis ? 1 : 0][c.sparse ? 1 : 0][gi] : nullptr;
+  if (slot) {
+    const int known = slot->load(std::memory_order_relaxed);
+    if (known > 0) return known;
+  }
   AttnPlan p{};
   p.group = group;
   int occ = 0;
   if (dispatch(c, p, nullptr, nullptr, nullptr, nullptr, &occ) != hipSuccess || occ < 1) occ = 1;
-  if (slot) *slot = occ;
+  if (slot) slot->store(occ, std::memory_order_relaxed);
   return occ;
 }
 
