@@ -187,7 +187,7 @@ def main():
     cu1 = torch.arange(s.batch + 1, dtype=torch.int32, device=dev)
     ones = [1] * s.batch
     out = torch.empty((s.batch, s.n_q_heads, s.d_head), dtype=torch.float32, device=dev)
-    ws = torch.empty(K.kvq_workspace_bytes(cfg, s.batch, T), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(K.kvq_workspace_bytes(cfg, s.batch, T), dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(s.d_head)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()

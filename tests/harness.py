@@ -39,6 +39,10 @@ class Pair:
         self.gpu = K.KVCache(K.Config.from_spec(s), s.batch, max_tokens)
         self.ref = RefCache(ref_config(s), s.batch, max_tokens) if with_ref else None
         self.T = max_tokens
+        # one workspace, zero-filled once and reused by every attention call
+        import torch
+        self.ws = torch.zeros(max(1, K.kvq_workspace_bytes(self.gpu.cfg, s.batch, max_tokens)),
+                              dtype=torch.uint8, device="cuda")
 
     def append(self, k, v, n):
         """k, v: fp16 numpy [N, H, D] packed by sequence."""
@@ -49,14 +53,12 @@ class Pair:
             self.ref.append(k, v, n)
         torch.cuda.synchronize()
 
-    def attend(self, q, scale=None):
+    def attend(self, q, scale=None, ws=None):
         import torch
         s = self.s
         scale = 1.0 / math.sqrt(s.d_head) if scale is None else scale
         out = torch.empty((self.B, s.n_q_heads, s.d_head), dtype=torch.float32, device="cuda")
-        ws = torch.empty(max(1, self.K.kvq_workspace_bytes(self.gpu.cfg, self.B, self.T)),
-                         dtype=torch.uint8, device="cuda")
-        self.K.kvq_decode_attention(self.gpu, to_dev(q), out, scale, ws)
+        self.K.kvq_decode_attention(self.gpu, to_dev(q), out, scale, self.ws if ws is None else ws)
         torch.cuda.synchronize()
         return out.cpu().numpy(), scale
 
