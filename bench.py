@@ -10,7 +10,9 @@ each step reads a cache that is not resident in the 256 MB last-level cache.
 Prints one JSON line: tokens/s (value), ms per step, and for the attention
 kernel a roofline entry (algorithmic bytes per launch / measured launch time
 against 8 TB/s HBM) plus the float64 oracle timed on the host as a reported
-baseline.
+baseline. An "append" entry reports the quantize-on-append path on its own:
+a whole-context prefill (GB/s over its algorithmic bytes) and the per-step
+append of one token per sequence.
 """
 import argparse
 import json
@@ -72,6 +74,26 @@ def recorded_traffic(cid):
     if not rec or rec.get("source_sha256_16") != attention_source_hash():
         return None
     return rec["traffic_bytes_per_dispatch"]
+
+
+def prefill_bytes(s, lens):
+    """Algorithmic bytes of quantizing a whole context on append: the fp16
+    keys and values read once, the packed cache (codes, metadata, residual
+    keys, sparse entries) written once."""
+    read = sum(lens) * s.n_kv_heads * s.d_head * 2 * 2
+    written = algorithmic_bytes(s, lens) - s.batch * s.n_q_heads * s.d_head * (2 + 4)
+    return read + written
+
+
+def append_report(s, lens, prefill_ms, step_ms):
+    """Quantize-on-append timings (HIP events on the launch stream): a whole
+    prefill of the workload's context, and the append of one token per
+    sequence inside each timed decode step (flushes included)."""
+    nbytes = prefill_bytes(s, lens)
+    pre_s = float(np.mean(prefill_ms)) / 1e3
+    return {"prefill_tokens": int(sum(lens)), "prefill_bytes": nbytes,
+            "prefill_us": pre_s * 1e6, "prefill_GBps": nbytes / pre_s / 1e9,
+            "decode_step_append_us": float(np.mean(step_ms)) * 1e3}
 
 
 def cpu_baseline(s, n_seq, steps):
@@ -163,15 +185,33 @@ def main():
     T = ((max(lens0) + per_rep + 31) // 32) * 32
     cfg = K.Config.from_spec(s)
 
-    # prefill one cache, then clone it into the replicas
+    # prefill one cache (untimed: first launches), then two more timed
+    # prefills into fresh caches (quantize-on-append of the whole context);
+    # the replicas are those caches and clones of the first
     ks, vs = zip(*[W.prefill(s, 0, b, lens0[b]) for b in range(s.batch)])
     cu = torch.tensor(np.concatenate([[0], np.cumsum(lens0)]).astype(np.int32), device=dev)
-    base = K.KVCache(cfg, s.batch, T)
-    K.kvq_append(base, torch.from_numpy(np.concatenate(ks)).to(dev),
-                 torch.from_numpy(np.concatenate(vs)).to(dev), cu, lens0)
+    kd = torch.from_numpy(np.concatenate(ks)).to(dev)
+    vd = torch.from_numpy(np.concatenate(vs)).to(dev)
     del ks, vs
+    base = K.KVCache(cfg, s.batch, T)
+    K.kvq_append(base, kd, vd, cu, lens0)
     reps = [base]
-    for _ in range(nrep - 1):
+    prefill_ms = []
+    for _ in range(2):
+        r = K.KVCache(cfg, s.batch, T)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        K.kvq_append(r, kd, vd, cu, lens0)
+        b.record()
+        torch.cuda.synchronize()
+        prefill_ms.append(a.elapsed_time(b))
+        if len(reps) < nrep:
+            reps.append(r)
+        else:
+            del r
+    del kd, vd
+    while len(reps) < nrep:
         r = K.KVCache(cfg, s.batch, T)
         r.copy_from(base)
         reps.append(r)
@@ -194,6 +234,8 @@ def main():
 
     def run(i, ev=None):
         r = reps[i % nrep]
+        if ev is not None:
+            ev[2].record(stream)
         K.kvq_append(r, kn[i % pool], vn[i % pool], cu1, ones, stream)
         if ev is not None:
             ev[0].record(stream)
@@ -211,7 +253,8 @@ def main():
         rr = i % nrep
         step_lens[rr] = [x + 1 for x in step_lens[rr]]
         lens_timed.append(list(step_lens[rr]))
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    # per timed step: attention start, attention end, append start
+    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -219,7 +262,8 @@ def main():
         run(args.warmup + j, events[j])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = [a.elapsed_time(b) for a, b in events]
+    attn_ms = [a.elapsed_time(b) for a, b, _ in events]
+    append_ms = [c.elapsed_time(a) for a, _, c in events]
     attn_avg_s = float(np.mean(attn_ms)) / 1e3
     bytes_avg = float(np.mean([algorithmic_bytes(s, L) for L in lens_timed]))
     achieved = bytes_avg / attn_avg_s / 1e9
@@ -251,6 +295,7 @@ def main():
                      "p10_p90_us": [float(np.percentile(attn_ms, 10)) * 1e3,
                                     float(np.percentile(attn_ms, 90)) * 1e3],
                      "algorithmic_bytes_per_launch": bytes_avg},
+        "append": append_report(s, lens0, prefill_ms, append_ms),
     }
     if not args.no_cpu_baseline:
         tps, threads, dt = cpu_baseline(s, min(args.cpu_seqs, s.batch), args.cpu_steps)

@@ -59,3 +59,15 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("cid", [2, 4, 5])
+def test_prefill_bytes_are_fp16_read_plus_cache_written(cid):
+    # a whole-context append reads every fp16 key and value once and writes
+    # the cache arrays once (full caches: no residual keys left)
+    s = replace(W.spec(cid), batch=2)
+    T = 512
+    sz = actual_bytes(ref_config(s), s.batch, T)
+    cache = sz["k_codes"] + sz["k_meta"] + sz["k_sparse"] + sz["v_codes"] + sz["v_meta"]
+    fp16_in = s.batch * T * s.n_kv_heads * s.d_head * 2 * 2
+    assert bench.prefill_bytes(s, [T] * s.batch) == fp16_in + cache
