@@ -76,6 +76,11 @@ def recorded_traffic(cid):
     return rec["traffic_bytes_per_dispatch"]
 
 
+def progress(msg):
+    """A line on stderr per stage (stdout carries only the result line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def prefill_bytes(s, lens):
     """Algorithmic bytes of quantizing a whole context on append: the fp16
     keys and values read once, the packed cache (codes, metadata, residual
@@ -188,6 +193,7 @@ def main():
     # prefill one cache (untimed: first launches), then two more timed
     # prefills into fresh caches (quantize-on-append of the whole context);
     # the replicas are those caches and clones of the first
+    progress(f"workload {s.cid}: generating {sum(lens0)} prefill tokens")
     ks, vs = zip(*[W.prefill(s, 0, b, lens0[b]) for b in range(s.batch)])
     cu = torch.tensor(np.concatenate([[0], np.cumsum(lens0)]).astype(np.int32), device=dev)
     kd = torch.from_numpy(np.concatenate(ks)).to(dev)
@@ -215,6 +221,7 @@ def main():
         r = K.KVCache(cfg, s.batch, T)
         r.copy_from(base)
         reps.append(r)
+    progress(f"{nrep} cache replicas ready; prefill {np.mean(prefill_ms) * 1e3:.1f} us")
 
     # per-step inputs resident on the device
     pool = 16
@@ -268,6 +275,7 @@ def main():
     bytes_avg = float(np.mean([algorithmic_bytes(s, L) for L in lens_timed]))
     achieved = bytes_avg / attn_avg_s / 1e9
 
+    progress(f"{args.steps} timed steps in {wall:.3f} s")
     ms_per_step = wall / args.steps * 1e3
     value = s.batch * args.steps / wall
     res = {
@@ -298,6 +306,7 @@ def main():
         "append": append_report(s, lens0, prefill_ms, append_ms),
     }
     if not args.no_cpu_baseline:
+        progress("timing the oracle on the host")
         tps, threads, dt = cpu_baseline(s, min(args.cpu_seqs, s.batch), args.cpu_steps)
         res["cpu_baseline"] = {
             "value": tps, "unit": "tokens/s", "cores": threads, "kind": "oracle",
