@@ -23,9 +23,16 @@ Sources (by page title and section):
             (per-channel keys, per-token values, fp residual, KVQuant's
             dense-and-sparse outliers); "Why 8 bits hides the problem and 4 bits
             exposes it" (2 bits = four levels).
+  [P3-fmt]  "KV Cache Quantization Benchmarked: 8-bit Is Nearly Lossless, How
+            Much Does 4-bit Cost?", the memory paragraph of "KV Cache
+            Quantization: 8-bit Is Essentially Free" (8-bit caches at about
+            32-34 KiB per token against 64 KiB) and the glossary paragraph
+            (fp8_e4m3: 4-bit exponent, 3-bit mantissa; q8_0 / q4_0: blocks
+            of 32 elements sharing a scale).
 
 Modules:
   quant   group quantize / dequantize, integer ranges, dense-and-sparse split
+  fp8     fp8 E4M3 elements: decoding from the bit layout, rounding encode
   cache   the cache state machine (append, residual flush), the documented
           packed byte layout, dequantized tensors, float64 attention, and the
           log-sum-exp merge of split partials (softmax_partial, merge_partials)

@@ -15,13 +15,18 @@ State per sequence b (identical for every KV head): L = tokens held.
     first gives up its k largest-|x| entries (quant.split_sparse); residual
     keys are never split.
 
-Logical arrays (host numpy): codes q as int8 per element, scales and zeros as
-fp16 per group, residual keys as fp16, sparse entries as (channel, fp16).
-``pack()`` turns them into the byte layout that include/kvq.h documents.
+  * fp8 E4M3 keys and values (oracle/fp8.py, [P3-fmt]): one code per element
+    with one fp32 scale per cache for keys and one for values; no groups, so
+    no metadata arrays. fp8 keys are on the token axis.
+
+Logical arrays (host numpy): codes q as int8 per element (fp8: the uint8
+codes), scales and zeros as fp16 per group, residual keys as fp16, sparse
+entries as (channel, fp16). ``pack()`` turns them into the byte layout that
+include/kvq.h documents.
 """
 import numpy as np
 
-from . import quant
+from . import fp8, quant
 
 F16 = np.float16
 BLOCK = 32  # tokens per per-channel key group and per value code block
@@ -32,7 +37,8 @@ class Config:
 
     def __init__(self, d_head=128, n_kv_heads=1, n_q_heads=1, k_bits=8, v_bits=8,
                  k_axis="token", k_group_tokens=0, k_residual_tokens=0,
-                 k_sparse_per_vector=0):
+                 k_sparse_per_vector=0, k_format="int", v_format="int",
+                 k_scale=1.0, v_scale=1.0):
         self.d_head = d_head
         self.n_kv_heads = n_kv_heads
         self.n_q_heads = n_q_heads
@@ -42,10 +48,22 @@ class Config:
         self.k_group_tokens = k_group_tokens
         self.k_residual_tokens = k_residual_tokens
         self.k_sparse_per_vector = k_sparse_per_vector
+        self.k_format = k_format          # "int" (affine codes) or "fp8" (E4M3)
+        self.v_format = v_format
+        self.k_scale = k_scale            # fp8 only: the per-cache fp32 scales
+        self.v_scale = v_scale
 
     @property
     def per_channel(self):
         return self.k_axis == "channel"
+
+    @property
+    def k_fp8(self):
+        return self.k_format == "fp8"
+
+    @property
+    def v_fp8(self):
+        return self.v_format == "fp8"
 
 
 class RefCache:
@@ -54,12 +72,15 @@ class RefCache:
         if cfg.per_channel:
             assert cfg.k_group_tokens == BLOCK
             assert cfg.k_residual_tokens > 0 and cfg.k_residual_tokens % BLOCK == 0
+            assert not cfg.k_fp8, "fp8 keys are on the token axis"
+        for f, bits in ((cfg.k_format, cfg.k_bits), (cfg.v_format, cfg.v_bits)):
+            assert f in ("int", "fp8") and (f == "int" or bits == 8)
         self.cfg = cfg
         self.B, self.T = batch, max_tokens
         H, D = cfg.n_kv_heads, cfg.d_head
         self.H, self.D = H, D
         self.length = np.zeros(batch, np.int64)
-        self.kq = np.zeros((batch, H, max_tokens, D), np.int8)
+        self.kq = np.zeros((batch, H, max_tokens, D), np.uint8 if cfg.k_fp8 else np.int8)
         if cfg.per_channel:
             nb = max_tokens // BLOCK
             self.ks = np.zeros((batch, H, nb, D), F16)
@@ -72,7 +93,7 @@ class RefCache:
         ksp = cfg.k_sparse_per_vector
         self.sp_col = np.zeros((batch, H, max_tokens, ksp), np.int64)
         self.sp_val = np.zeros((batch, H, max_tokens, ksp), F16)
-        self.vq = np.zeros((batch, H, max_tokens, D), np.int8)
+        self.vq = np.zeros((batch, H, max_tokens, D), np.uint8 if cfg.v_fp8 else np.int8)
         self.vs = np.zeros((batch, H, max_tokens), F16)
         self.vz = np.zeros((batch, H, max_tokens), F16)
 
@@ -101,12 +122,18 @@ class RefCache:
                 raise ValueError("capacity")
             if n == 0:
                 continue
-            # values: one group per (head, token) over the D channels
-            q, s, z = quant.quantize_groups(vb, cfg.v_bits)
-            self.vq[b, :, L:L + n] = q
-            self.vs[b, :, L:L + n] = s
-            self.vz[b, :, L:L + n] = z
-            if not cfg.per_channel:
+            # values: one group per (head, token) over the D channels; fp8:
+            # one code per element
+            if cfg.v_fp8:
+                self.vq[b, :, L:L + n] = fp8.quantize(vb, cfg.v_scale)
+            else:
+                q, s, z = quant.quantize_groups(vb, cfg.v_bits)
+                self.vq[b, :, L:L + n] = q
+                self.vs[b, :, L:L + n] = s
+                self.vz[b, :, L:L + n] = z
+            if cfg.k_fp8:
+                self.kq[b, :, L:L + n] = fp8.quantize(kb, cfg.k_scale)
+            elif not cfg.per_channel:
                 q, s, z = quant.quantize_groups(kb, cfg.k_bits)
                 self.kq[b, :, L:L + n] = q
                 self.ks[b, :, L:L + n] = s
@@ -147,6 +174,8 @@ class RefCache:
         x_hat = s*(q - z), plus the sparse entries added back, then the fp16
         residual keys verbatim."""
         L, Q = int(self.length[b]), self.n_quantized(b)
+        if self.cfg.k_fp8:
+            return _fp8_hat(self.kq[b, h, :L], self.cfg.k_scale, dtype)
         deq = quant.dequantize_f64 if dtype == np.float64 else quant.dequantize
         if self.cfg.per_channel:
             blk = np.arange(Q) // BLOCK
@@ -161,6 +190,8 @@ class RefCache:
 
     def v_hat(self, b, h, dtype=np.float64):
         L = int(self.length[b])
+        if self.cfg.v_fp8:
+            return _fp8_hat(self.vq[b, h, :L], self.cfg.v_scale, dtype)
         deq = quant.dequantize_f64 if dtype == np.float64 else quant.dequantize
         return deq(self.vq[b, h, :L], self.vs[b, h, :L, None], self.vz[b, h, :L, None])
 
@@ -208,8 +239,9 @@ class RefCache:
         not fixed by the pages)."""
         cfg = self.cfg
         B, H, T, D = self.B, self.H, self.T, self.D
-        kqmin = quant.qrange(cfg.k_bits)[0]
-        vqmin = quant.qrange(cfg.v_bits)[0]
+        # stored code = q - q_min for integer codes, the code itself for fp8
+        kqmin = 0 if cfg.k_fp8 else quant.qrange(cfg.k_bits)[0]
+        vqmin = 0 if cfg.v_fp8 else quant.qrange(cfg.v_bits)[0]
         # stored unsigned codes; token slots without a code stay 0
         ku = np.zeros((B, H, T, D), np.uint8)
         vu = np.zeros((B, H, T, D), np.uint8)
@@ -223,7 +255,8 @@ class RefCache:
         out["k_codes"] = pack_fields(ku, cfg.k_bits)                       # [B,H,T,D*kb/8]
         vblk = vu.reshape(B, H, T // BLOCK, BLOCK, D).transpose(0, 1, 2, 4, 3)
         out["v_codes"] = pack_fields(vblk, cfg.v_bits)                     # [B,H,T/32,D,4*vb]
-        out["v_meta"] = meta_words(self.vs, self.vz)
+        if not cfg.v_fp8:
+            out["v_meta"] = meta_words(self.vs, self.vz)
         if cfg.per_channel:
             out["k_meta"] = meta_words(self.ks, self.kz)                   # [B,H,T/32,D]
             out["k_resid"] = quant.f16_bits(self.kres)
@@ -237,9 +270,17 @@ class RefCache:
                 for b in range(B):
                     sp[b, :, kmeta_len[b]:] = 0
                 out["k_sparse"] = sp
-        else:
+        elif not cfg.k_fp8:
             out["k_meta"] = meta_words(self.ks, self.kz)                   # [B,H,T]
         return out
+
+
+def _fp8_hat(codes, scale, dtype):
+    """scale * value(code): exact in float64; in float32 the product rounded
+    once (the value kvq_dequantize rounds to fp16)."""
+    if dtype == np.float64:
+        return fp8.dequantize_f64(codes, scale)
+    return np.float32(scale) * fp8.e4m3_value(codes).astype(np.float32)
 
 
 def pack_fields(u, bits):
