@@ -3,7 +3,9 @@
 
 One step = one pass of the hot path over one batch: quantize-on-append of one
 new key/value token per sequence (with the residual flush when a window fills)
-followed by fused-dequant decode attention for one query token per sequence.
+followed by fused-dequant decode attention for one query token per sequence,
+in every layer of the workload (the 32-layer worked-example shape runs all
+32 layers per step; the roofline entry is per attention launch, one layer).
 Inputs are resident in HBM before timing starts. Cache replicas are rotated so
 each step reads a cache that is not resident in the 256 MB last-level cache.
 
@@ -178,27 +180,32 @@ def main():
         copy_probe()
         return
     s = W.spec(args.config)
-    if s.layers != 1:
-        raise SystemExit("bench.py times single-layer workloads")
     torch.cuda.set_device(0)
     dev = "cuda"
     lens0 = [int(x) for x in W.seq_lengths(s)]
     cache_bytes = algorithmic_bytes(s, lens0)
-    nrep = args.replicas or max(1, min(16, math.ceil(1.25e9 / cache_bytes)))
+    nlay = s.layers
+    # single-layer workloads rotate cache replicas so that each step misses
+    # the last-level cache; a multi-layer workload visits every layer's cache
+    # in each step, which already exceeds it
+    nrep = 1 if nlay > 1 else (args.replicas or max(1, min(16, math.ceil(1.25e9 / cache_bytes))))
     total_steps = args.warmup + args.steps
     per_rep = math.ceil(total_steps / nrep)
     T = ((max(lens0) + per_rep + 31) // 32) * 32
     cfg = K.Config.from_spec(s)
-
-    # prefill one cache (untimed: first launches), then two more timed
-    # prefills into fresh caches (quantize-on-append of the whole context);
-    # the replicas are those caches and clones of the first
-    progress(f"workload {s.cid}: generating {sum(lens0)} prefill tokens")
-    ks, vs = zip(*[W.prefill(s, 0, b, lens0[b]) for b in range(s.batch)])
     cu = torch.tensor(np.concatenate([[0], np.cumsum(lens0)]).astype(np.int32), device=dev)
-    kd = torch.from_numpy(np.concatenate(ks)).to(dev)
-    vd = torch.from_numpy(np.concatenate(vs)).to(dev)
-    del ks, vs
+
+    def prefill_inputs(layer):
+        ks, vs = zip(*[W.prefill(s, layer, b, lens0[b]) for b in range(s.batch)])
+        return (torch.from_numpy(np.concatenate(ks)).to(dev),
+                torch.from_numpy(np.concatenate(vs)).to(dev))
+
+    # prefill layer 0's cache (untimed: first launches), then two more timed
+    # prefills into fresh caches (quantize-on-append of the whole context);
+    # the replicas are those caches and clones of the first; further layers
+    # get caches of their own
+    progress(f"workload {s.cid}: generating {sum(lens0)} prefill tokens x {nlay} layer(s)")
+    kd, vd = prefill_inputs(0)
     base = K.KVCache(cfg, s.batch, T)
     K.kvq_append(base, kd, vd, cu, lens0)
     reps = [base]
@@ -221,16 +228,27 @@ def main():
         r = K.KVCache(cfg, s.batch, T)
         r.copy_from(base)
         reps.append(r)
-    progress(f"{nrep} cache replicas ready; prefill {np.mean(prefill_ms) * 1e3:.1f} us")
+    layer_caches = [base]
+    for layer in range(1, nlay):
+        kd, vd = prefill_inputs(layer)
+        c = K.KVCache(cfg, s.batch, T)
+        K.kvq_append(c, kd, vd, cu, lens0)
+        layer_caches.append(c)
+        del kd, vd
+        torch.cuda.synchronize()
+    progress(f"{nrep} cache replica(s) x {nlay} layer(s) ready; prefill {np.mean(prefill_ms) * 1e3:.1f} us")
 
-    # per-step inputs resident on the device
-    pool = 16
-    qs, kn, vn = [], [], []
-    for i in range(pool):
-        q, k, v = W.step(s, 0, i)
-        qs.append(torch.from_numpy(q).to(dev))
-        kn.append(torch.from_numpy(k).to(dev))
-        vn.append(torch.from_numpy(v).to(dev))
+    # per-step inputs resident on the device, per layer
+    pool = 16 if nlay == 1 else 4
+    inputs = []
+    for layer in range(nlay):
+        qs, kn, vn = [], [], []
+        for i in range(pool):
+            q, k, v = W.step(s, layer, i)
+            qs.append(torch.from_numpy(q).to(dev))
+            kn.append(torch.from_numpy(k).to(dev))
+            vn.append(torch.from_numpy(v).to(dev))
+        inputs.append((qs, kn, vn))
     cu1 = torch.arange(s.batch + 1, dtype=torch.int32, device=dev)
     ones = [1] * s.batch
     out = torch.empty((s.batch, s.n_q_heads, s.d_head), dtype=torch.float32, device=dev)
@@ -239,29 +257,37 @@ def main():
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
-    def run(i, ev=None):
-        r = reps[i % nrep]
-        if ev is not None:
-            ev[2].record(stream)
-        K.kvq_append(r, kn[i % pool], vn[i % pool], cu1, ones, stream)
-        if ev is not None:
-            ev[0].record(stream)
-        K.kvq_decode_attention(r, qs[i % pool], out, scale, ws, stream)
-        if ev is not None:
-            ev[1].record(stream)
+    def step_caches(i):
+        """(layer, cache) pairs one decode step visits, in order."""
+        if nlay > 1:
+            return list(enumerate(layer_caches))
+        return [(0, reps[i % nrep])]
+
+    def run(i, evs=None):
+        for u, (layer, r) in enumerate(step_caches(i)):
+            qs, kn, vn = inputs[layer]
+            if evs is not None:
+                evs[u][2].record(stream)
+            K.kvq_append(r, kn[i % pool], vn[i % pool], cu1, ones, stream)
+            if evs is not None:
+                evs[u][0].record(stream)
+            K.kvq_decode_attention(r, qs[i % pool], out, scale, ws, stream)
+            if evs is not None:
+                evs[u][1].record(stream)
 
     for i in range(args.warmup):
         run(i)
     torch.cuda.synchronize()
-    # lengths seen by the timed attention launches
+    # lengths seen by the timed attention launches (every layer of a step
+    # holds the same lengths)
     lens_timed = []
     step_lens = [list(r.len_host) for r in reps]
     for i in range(args.warmup, total_steps):
         rr = i % nrep
         step_lens[rr] = [x + 1 for x in step_lens[rr]]
-        lens_timed.append(list(step_lens[rr]))
-    # per timed step: attention start, attention end, append start
-    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+        lens_timed += [list(step_lens[rr])] * nlay
+    # per attention launch: attention start, attention end, append start
+    events = [[tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(nlay)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -269,8 +295,9 @@ def main():
         run(args.warmup + j, events[j])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = [a.elapsed_time(b) for a, b, _ in events]
-    append_ms = [c.elapsed_time(a) for a, _, c in events]
+    launches = [e for step in events for e in step]
+    attn_ms = [a.elapsed_time(b) for a, b, _ in launches]
+    append_ms = [c.elapsed_time(a) for a, _, c in launches]
     attn_avg_s = float(np.mean(attn_ms)) / 1e3
     bytes_avg = float(np.mean([algorithmic_bytes(s, L) for L in lens_timed]))
     achieved = bytes_avg / attn_avg_s / 1e9
@@ -295,7 +322,7 @@ def main():
                    "n_kv_heads": s.n_kv_heads, "d_head": s.d_head, "seq_len": s.seq_len,
                    "k_bits": s.k_bits, "v_bits": s.v_bits, "k_axis": s.k_axis,
                    "k_group": s.k_group, "k_residual": s.k_residual, "k_sparse": s.k_sparse,
-                   "cache_replicas": nrep},
+                   "layers": nlay, "cache_replicas": nrep},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBS, "traffic": recorded_traffic(args.config),
                      "kernel": "kvq_decode_attention (attention + split merge)",
@@ -308,10 +335,11 @@ def main():
     if not args.no_cpu_baseline:
         progress("timing the oracle on the host")
         tps, threads, dt = cpu_baseline(s, min(args.cpu_seqs, s.batch), args.cpu_steps)
+        per_layer = f", one of {nlay} layers, rate divided by {nlay}" if nlay > 1 else ""
         res["cpu_baseline"] = {
-            "value": tps, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "value": tps / nlay, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{min(args.cpu_seqs, s.batch)} of {s.batch} sequences x {args.cpu_steps} "
-                      f"decode steps (append + float64 attention), {dt:.1f} s"}
+                      f"decode steps (append + float64 attention){per_layer}, {dt:.1f} s"}
     print(json.dumps(res), flush=True)
 
 
