@@ -71,3 +71,71 @@ def test_prefill_bytes_are_fp16_read_plus_cache_written(cid):
     cache = sz["k_codes"] + sz["k_meta"] + sz["k_sparse"] + sz["v_codes"] + sz["v_meta"]
     fp16_in = s.batch * T * s.n_kv_heads * s.d_head * 2 * 2
     assert bench.prefill_bytes(s, [T] * s.batch) == fp16_in + cache
+
+
+class _Event:
+    """Stand-in for torch.cuda.Event: record() stamps a fake clock 10 us ahead."""
+    clock = 0.0
+
+    def __init__(self, enable_timing=False):
+        self.t = None
+
+    def record(self, stream=None):
+        _Event.clock += 0.01
+        self.t = _Event.clock
+
+    def elapsed_time(self, other):
+        return other.t - self.t
+
+
+class _Cache:
+    def __init__(self, cfg, batch, max_tokens, device="cuda"):
+        self.batch, self.max_tokens = batch, max_tokens
+        self.len_host = [0] * batch
+
+    def copy_from(self, other):
+        self.len_host = list(other.len_host)
+
+
+@pytest.mark.parametrize("argv", [["--config", "1", "--steps", "5", "--warmup", "2", "--cpu-steps", "1"],
+                                  ["--config", "2", "--steps", "3", "--warmup", "2", "--no-cpu-baseline"]])
+def test_bench_main_with_gpu_calls_stubbed(argv, monkeypatch, capsys):
+    """bench.main() end to end on the CPU, every GPU call replaced by a stub:
+    the data flow (replicas, lengths, events, byte counts) and the JSON line."""
+    import json
+    import torch
+    import quantized_decode_attention_03_amd as K
+
+    monkeypatch.setattr(torch.cuda, "Event", _Event)
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: None)
+    monkeypatch.setattr(torch.cuda, "set_device", lambda *a, **k: None)
+    monkeypatch.setattr(torch.cuda, "current_stream", lambda *a, **k: None)
+    monkeypatch.setattr(torch.Tensor, "to", lambda self, *a, **k: self)
+    for fn in ("zeros", "empty", "tensor", "arange"):
+        orig = getattr(torch, fn)
+        monkeypatch.setattr(torch, fn, (lambda o: lambda *a, **k: o(*a, **{x: y for x, y in k.items()
+                                                                             if x != "device"}))(orig))
+
+    def append(c, k, v, cu, n, stream=None):
+        c.len_host = [a + int(b) for a, b in zip(c.len_host, n)]
+
+    monkeypatch.setattr(K, "KVCache", _Cache)
+    monkeypatch.setattr(K, "kvq_append", append)
+    monkeypatch.setattr(K, "kvq_decode_attention", lambda *a, **k: None)
+    monkeypatch.setattr(sys, "argv", ["bench.py"] + argv)
+    bench.main()
+    line = capsys.readouterr().out.strip().splitlines()[-1]
+    d = json.loads(line)
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config", "roofline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["unit"] == "tokens/s" and d["value"] > 0
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
+    assert r["frac"] == pytest.approx(r["achieved"] / r["peak"])
+    s = W.spec(int(argv[1]))
+    assert r["algorithmic_bytes_per_launch"] >= bench.algorithmic_bytes(s, [int(x) for x in W.seq_lengths(s)])
+    assert d["append"]["prefill_bytes"] == bench.prefill_bytes(s, [int(x) for x in W.seq_lengths(s)])
+    assert ("cpu_baseline" in d) == ("--no-cpu-baseline" not in argv)
+    if "cpu_baseline" in d:
+        assert d["cpu_baseline"]["kind"] == "oracle" and d["cpu_baseline"]["value"] > 0
