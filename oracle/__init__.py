@@ -31,9 +31,11 @@ Sources (by page title and section):
             of 32 elements sharing a scale).
 
 Modules:
-  quant   group quantize / dequantize, integer ranges, dense-and-sparse split
+  quant   group quantize / dequantize (affine and symmetric), integer ranges,
+          dense-and-sparse split
   fp8     fp8 E4M3 elements: decoding from the bit layout, rounding encode
-  cache   the cache state machine (append, residual flush), the documented
+  cache   the cache state machine (append, residual flush; affine, fp8 and
+          symmetric 32-element block formats), the documented
           packed byte layout, dequantized tensors, float64 attention, and the
           log-sum-exp merge of split partials (softmax_partial, merge_partials)
   sizes   the bytes-per-token formula and the actual cache sizes

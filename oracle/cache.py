@@ -18,6 +18,11 @@ State per sequence b (identical for every KV head): L = tokens held.
   * fp8 E4M3 keys and values (oracle/fp8.py, [P3-fmt]): one code per element
     with one fp32 scale per cache for keys and one for values; no groups, so
     no metadata arrays. fp8 keys are on the token axis.
+  * Symmetric 32-element blocks ("sym32"; [P2-int] "Symmetric vs asymmetric",
+    [P3-fmt]'s q8_0 / q4_0 blocks of 32 elements sharing a scale): each token
+    vector is cut into 4 blocks of 32 consecutive channels, each quantized
+    symmetrically (quant.quantize_sym_groups) with one fp16 scale. Keys on the
+    token axis.
 
 Logical arrays (host numpy): codes q as int8 per element (fp8: the uint8
 codes), scales and zeros as fp16 per group, residual keys as fp16, sparse
@@ -48,7 +53,8 @@ class Config:
         self.k_group_tokens = k_group_tokens
         self.k_residual_tokens = k_residual_tokens
         self.k_sparse_per_vector = k_sparse_per_vector
-        self.k_format = k_format          # "int" (affine codes) or "fp8" (E4M3)
+        self.k_format = k_format          # "int" (affine codes), "fp8" (E4M3) or
+                                          # "sym32" (symmetric 32-channel blocks)
         self.v_format = v_format
         self.k_scale = k_scale            # fp8 only: the per-cache fp32 scales
         self.v_scale = v_scale
@@ -65,6 +71,14 @@ class Config:
     def v_fp8(self):
         return self.v_format == "fp8"
 
+    @property
+    def k_sym(self):
+        return self.k_format == "sym32"
+
+    @property
+    def v_sym(self):
+        return self.v_format == "sym32"
+
 
 class RefCache:
     def __init__(self, cfg, batch, max_tokens):
@@ -72,9 +86,9 @@ class RefCache:
         if cfg.per_channel:
             assert cfg.k_group_tokens == BLOCK
             assert cfg.k_residual_tokens > 0 and cfg.k_residual_tokens % BLOCK == 0
-            assert not cfg.k_fp8, "fp8 keys are on the token axis"
+            assert not cfg.k_fp8 and not cfg.k_sym, "fp8 and block keys are on the token axis"
         for f, bits in ((cfg.k_format, cfg.k_bits), (cfg.v_format, cfg.v_bits)):
-            assert f in ("int", "fp8") and (f == "int" or bits == 8)
+            assert f in ("int", "fp8", "sym32") and (f != "fp8" or bits == 8)
         self.cfg = cfg
         self.B, self.T = batch, max_tokens
         H, D = cfg.n_kv_heads, cfg.d_head
@@ -86,6 +100,10 @@ class RefCache:
             self.ks = np.zeros((batch, H, nb, D), F16)
             self.kz = np.zeros((batch, H, nb, D), F16)
             self.kres = np.zeros((batch, H, cfg.k_residual_tokens, D), F16)
+        elif cfg.k_sym:
+            self.ks = np.zeros((batch, H, max_tokens, D // SYM_BLOCK), F16)
+            self.kz = None
+            self.kres = None
         else:
             self.ks = np.zeros((batch, H, max_tokens), F16)
             self.kz = np.zeros((batch, H, max_tokens), F16)
@@ -94,8 +112,12 @@ class RefCache:
         self.sp_col = np.zeros((batch, H, max_tokens, ksp), np.int64)
         self.sp_val = np.zeros((batch, H, max_tokens, ksp), F16)
         self.vq = np.zeros((batch, H, max_tokens, D), np.uint8 if cfg.v_fp8 else np.int8)
-        self.vs = np.zeros((batch, H, max_tokens), F16)
-        self.vz = np.zeros((batch, H, max_tokens), F16)
+        if cfg.v_sym:
+            self.vs = np.zeros((batch, H, max_tokens, D // SYM_BLOCK), F16)
+            self.vz = None
+        else:
+            self.vs = np.zeros((batch, H, max_tokens), F16)
+            self.vz = np.zeros((batch, H, max_tokens), F16)
 
     # ------------------------------------------------------------------ state
     def n_quantized(self, b):
@@ -126,6 +148,8 @@ class RefCache:
             # one code per element
             if cfg.v_fp8:
                 self.vq[b, :, L:L + n] = fp8.quantize(vb, cfg.v_scale)
+            elif cfg.v_sym:
+                self.vq[b, :, L:L + n], self.vs[b, :, L:L + n] = _sym_blocks(vb, cfg.v_bits)
             else:
                 q, s, z = quant.quantize_groups(vb, cfg.v_bits)
                 self.vq[b, :, L:L + n] = q
@@ -133,6 +157,8 @@ class RefCache:
                 self.vz[b, :, L:L + n] = z
             if cfg.k_fp8:
                 self.kq[b, :, L:L + n] = fp8.quantize(kb, cfg.k_scale)
+            elif cfg.k_sym:
+                self.kq[b, :, L:L + n], self.ks[b, :, L:L + n] = _sym_blocks(kb, cfg.k_bits)
             elif not cfg.per_channel:
                 q, s, z = quant.quantize_groups(kb, cfg.k_bits)
                 self.kq[b, :, L:L + n] = q
@@ -176,6 +202,8 @@ class RefCache:
         L, Q = int(self.length[b]), self.n_quantized(b)
         if self.cfg.k_fp8:
             return _fp8_hat(self.kq[b, h, :L], self.cfg.k_scale, dtype)
+        if self.cfg.k_sym:
+            return _sym_hat(self.kq[b, h, :L], self.ks[b, h, :L], dtype)
         deq = quant.dequantize_f64 if dtype == np.float64 else quant.dequantize
         if self.cfg.per_channel:
             blk = np.arange(Q) // BLOCK
@@ -192,6 +220,8 @@ class RefCache:
         L = int(self.length[b])
         if self.cfg.v_fp8:
             return _fp8_hat(self.vq[b, h, :L], self.cfg.v_scale, dtype)
+        if self.cfg.v_sym:
+            return _sym_hat(self.vq[b, h, :L], self.vs[b, h, :L], dtype)
         deq = quant.dequantize_f64 if dtype == np.float64 else quant.dequantize
         return deq(self.vq[b, h, :L], self.vs[b, h, :L, None], self.vz[b, h, :L, None])
 
@@ -255,7 +285,9 @@ class RefCache:
         out["k_codes"] = pack_fields(ku, cfg.k_bits)                       # [B,H,T,D*kb/8]
         vblk = vu.reshape(B, H, T // BLOCK, BLOCK, D).transpose(0, 1, 2, 4, 3)
         out["v_codes"] = pack_fields(vblk, cfg.v_bits)                     # [B,H,T/32,D,4*vb]
-        if not cfg.v_fp8:
+        if cfg.v_sym:
+            out["v_meta"] = quant.f16_bits(self.vs)                        # [B,H,T,4] scales
+        elif not cfg.v_fp8:
             out["v_meta"] = meta_words(self.vs, self.vz)
         if cfg.per_channel:
             out["k_meta"] = meta_words(self.ks, self.kz)                   # [B,H,T/32,D]
@@ -270,9 +302,30 @@ class RefCache:
                 for b in range(B):
                     sp[b, :, kmeta_len[b]:] = 0
                 out["k_sparse"] = sp
+        elif cfg.k_sym:
+            out["k_meta"] = quant.f16_bits(self.ks)                        # [B,H,T,4] scales
         elif not cfg.k_fp8:
             out["k_meta"] = meta_words(self.ks, self.kz)                   # [B,H,T]
         return out
+
+
+SYM_BLOCK = 32  # channels per symmetric block
+
+
+def _sym_blocks(x16, bits):
+    """x16 fp16 [H, n, D] -> (codes int8 [H, n, D], scales fp16 [H, n, D/32]):
+    each token vector cut into blocks of 32 consecutive channels."""
+    H, n, D = x16.shape
+    q, s = quant.quantize_sym_groups(x16.reshape(H, n, D // SYM_BLOCK, SYM_BLOCK), bits)
+    return q.reshape(H, n, D), s
+
+
+def _sym_hat(q, s16, dtype):
+    """scale of each element's block * code, [L, D]; exact in float64 and in
+    float32."""
+    L, D = q.shape
+    s = np.repeat(np.asarray(s16, F16).astype(dtype), SYM_BLOCK, axis=-1)
+    return s * np.asarray(q).astype(dtype)
 
 
 def _fp8_hat(codes, scale, dtype):

@@ -22,6 +22,11 @@ Readings where the page is silent (each is also listed in the design notes):
   * The zero-point is stored as fp16 and clamped to [-2048, 2048], the range in
     which every integer is an fp16.
   * int2 uses [-2, 1] (two's complement, the four levels of [P1-kivi]).
+
+Symmetric groups ([P2-int] "Symmetric vs asymmetric") force the zero point to
+zero: scale = max|x| / q_max (the range [-q_max, q_max] centred on zero),
+stored as fp16 rounded up, q = clamp(round(x / scale), -q_max, q_max) and
+x_hat = scale * q; an all-zero group takes scale 1.
 """
 import numpy as np
 
@@ -113,6 +118,41 @@ def dequantize_f64(q, s16, z16):
     """The same value as dequantize(), computed in float64."""
     return np.asarray(s16, dtype=F16).astype(np.float64) * (
         np.asarray(q).astype(np.float64) - np.asarray(z16, dtype=F16).astype(np.float64))
+
+
+def sym_qmax(bits):
+    """Largest code of the symmetric range [-q_max, q_max] centred on zero:
+    127, 7, 1 for 8, 4, 2 bits."""
+    return qrange(bits)[1]
+
+
+def sym_scale(amax, bits):
+    """Scale of symmetric groups ([P2-int] "Symmetric vs asymmetric": zero
+    point forced to zero, the integer range centred on real zero), with the
+    readings: scale = max|x| / q_max rounded up to fp16 (as for the affine
+    scale, so that every element stays within scale/2), and scale 1 for an
+    all-zero group. Returns fp16 scales."""
+    amax = np.asarray(amax, dtype=F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s16 = f32_to_f16_up(amax / F32(sym_qmax(bits)))
+    return np.where(amax == 0, F16(1.0), s16).astype(F16)
+
+
+def quantize_sym_groups(x16, bits):
+    """Symmetric quantization of groups along the last axis: q =
+    clamp(round(x / scale), -q_max, q_max), no zero point.
+    Returns (q int8 [..., n], s16 fp16 [...])."""
+    x = np.asarray(x16, dtype=F16).astype(F32)
+    qm = F32(sym_qmax(bits))
+    s16 = sym_scale(np.abs(x).max(axis=-1), bits)
+    q = np.clip(np.rint(x / s16.astype(F32)[..., None]), -qm, qm)
+    return q.astype(np.int8), s16
+
+
+def dequantize_sym(q, s16):
+    """x_hat = scale * q: one multiply, exact in fp32 (at most 8 + 11
+    significant bits)."""
+    return np.asarray(s16, dtype=F16).astype(F32) * np.asarray(q).astype(F32)
 
 
 def split_sparse(x16, k):

@@ -6,7 +6,8 @@ the nominal figure leaves out (the group scales, [P2-gran] last sentences;
 the sparse outlier store, [P1-kivi] table note): one 4-byte scale+zero word
 per group, the fp16 residual window and the sparse entries. fp8 E4M3 codes
 ([P3-fmt]) have no groups and so no metadata: their actual size is the
-nominal one.
+nominal one. Symmetric 32-element blocks carry one fp16 scale per block
+(2 bytes per 32 elements).
 """
 
 BLOCK = 32
@@ -27,10 +28,11 @@ def actual_bytes(cfg, batch, max_tokens):
     H, D, T = cfg.n_kv_heads, cfg.d_head, max_tokens
     n = batch * H
     fp8_k, fp8_v = cfg.k_fp8, cfg.v_fp8
+    blocks = D // BLOCK                           # sym32: one fp16 scale per 32 channels
     out = {
         "k_codes": n * T * D * cfg.k_bits // 8,
         "v_codes": n * T * D * cfg.v_bits // 8,
-        "v_meta": 0 if fp8_v else n * T * 4,      # fp8: no groups, no metadata
+        "v_meta": 0 if fp8_v else (n * T * blocks * 2 if cfg.v_sym else n * T * 4),
         "seq_len": batch * 4,
     }
     if cfg.per_channel:
@@ -38,7 +40,7 @@ def actual_bytes(cfg, batch, max_tokens):
         out["k_resid"] = n * cfg.k_residual_tokens * D * 2
         out["k_sparse"] = n * T * 8 if cfg.k_sparse_per_vector else 0
     else:
-        out["k_meta"] = 0 if fp8_k else n * T * 4
+        out["k_meta"] = 0 if fp8_k else (n * T * blocks * 2 if cfg.k_sym else n * T * 4)
         out["k_resid"] = 0
         out["k_sparse"] = 0
     out["nominal_bytes"] = batch * nominal_bytes_mixed(1, H, D, T, cfg.k_bits, cfg.v_bits)
