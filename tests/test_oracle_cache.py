@@ -22,6 +22,12 @@ def _cfg(kind, H=2, Hq=4):
         return Config(128, H, Hq, 2, 2, "channel", 32, 128, 0)
     if kind == "chan4sp":
         return Config(128, H, Hq, 4, 4, "channel", 32, 32, 2)
+    if kind == "fp8":
+        return Config(128, H, Hq, 8, 8, "token", k_format="fp8", v_format="fp8",
+                      k_scale=0.5, v_scale=2.0)
+    if kind.startswith("sym"):
+        b = int(kind[3:])
+        return Config(128, H, Hq, b, b, "token", k_format="sym32", v_format="sym32")
     raise KeyError(kind)
 
 
@@ -32,7 +38,7 @@ def _rand_kv(rng, n, H):
     return k.astype(np.float16), v.astype(np.float16)
 
 
-@pytest.mark.parametrize("kind", ["token8", "chan4", "chan2r128", "chan4sp"])
+@pytest.mark.parametrize("kind", ["token8", "chan4", "chan2r128", "chan4sp", "fp8", "sym8", "sym4", "sym2"])
 def test_bulk_append_equals_single_appends(kind):
     """Appending n keys at once reaches the same state as n single-token
     appends (the residual window fills and flushes the same way)."""
@@ -122,6 +128,22 @@ def test_dequantize_f16_matches_stdlib_half_rounding():
     assert np.all(kd[0, 70:] == 0) and np.all(vd[0, 70:] == 0)
     # residual keys (64..69) come back verbatim
     assert np.array_equal(quant.f16_bits(kd[0, 64:70]), quant.f16_bits(k[64:70]))
+
+
+def test_dequantize_f16_of_blocks_matches_stdlib_half_rounding():
+    """The symmetric blocks' fp16 values: s * q (exact) rounded to fp16 by the
+    standard library's IEEE half conversion."""
+    c = RefCache(_cfg("sym4"), 1, 64)
+    rng = np.random.default_rng(15)
+    k, v = _rand_kv(rng, 40, 2)
+    c.append(k, v, [40])
+    kd, vd = c.dequantize_f16()
+    k64 = c.k_hat(0, 0, np.float64)
+    for t in range(0, 40, 3):
+        for ch in range(0, 128, 7):
+            want = struct.unpack("<e", struct.pack("<e", float(k64[t, ch])))[0]
+            assert float(kd[0, t, 0, ch]) == want
+    assert np.all(kd[0, 40:] == 0) and np.all(vd[0, 40:] == 0)
 
 
 def test_pack_unpack_identity():
