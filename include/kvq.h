@@ -98,6 +98,13 @@
  *   caller (same stream). Asynchronous device faults surface at the caller's
  *   next synchronization.
  *
+ * Environment (read by the library; both optional)
+ *   KVQ_DEBUG=1         synchronize after every launch and print HIP errors.
+ *   KVQ_SPLIT_TOKENS=n  force the split length of kvq_decode_attention to n
+ *                       tokens (rounded up to a multiple of 32, at least 256)
+ *                       instead of the built-in plan; for checks that vary the
+ *                       split count on one input.
+ *
  * Errors
  *   Arguments are validated on the host before anything is launched; an error
  *   status means nothing was enqueued and no host state changed. KVQ_EHIP is

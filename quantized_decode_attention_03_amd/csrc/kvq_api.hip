@@ -96,6 +96,18 @@ int plan_tiles_per_split(const kvq_cache* cache, int n_kv_heads, int64_t slots) 
   return best_tps;
 }
 
+// Split length forced through the environment (KVQ_SPLIT_TOKENS, read on
+// every call), for checks that vary the split count on one input; 0 when
+// unset. Never below kMinSplitTokens, so the workspace bound still holds.
+int split_override_tiles() {
+  const char* e = getenv("KVQ_SPLIT_TOKENS");
+  if (!e || !*e) return 0;
+  const long v = strtol(e, nullptr, 10);
+  if (v <= 0) return 0;
+  const long tiles = std::max<long>((v + kBlock - 1) / kBlock, kMinSplitTiles);
+  return (int)std::min<long>(tiles, 1L << 20);
+}
+
 kvq_status check_config(const kvq_config* cfg) {
   if (!cfg) return KVQ_EINVAL;
   if (cfg->n_kv_heads < 1 || cfg->n_q_heads < 1) return KVQ_EINVAL;
@@ -257,8 +269,9 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   p.Hq = cfg->n_q_heads;
   p.group = cfg->n_q_heads / cfg->n_kv_heads;
   p.scale = softmax_scale;
-  const int tps = plan_tiles_per_split(cache, cfg->n_kv_heads,
-                                       compute_units() * attention_blocks_per_cu(v, p.group));
+  int tps = plan_tiles_per_split(cache, cfg->n_kv_heads,
+                                 compute_units() * attention_blocks_per_cu(v, p.group));
+  if (const int forced = split_override_tiles()) tps = forced;
   int lmax = 0;
   for (int b = 0; b < cache->batch; ++b) lmax = std::max(lmax, (int)cache->len_host[b]);
   p.tokens_per_split = tps * kBlock;

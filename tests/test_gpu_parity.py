@@ -123,7 +123,7 @@ def test_attention_deterministic(cid):
     p.append(k, v, lens)
     q, _, _ = W.step(s, 0, 0)
     first, _ = p.attend(q)
-    for _ in range(5):
+    for _ in range(9):                     # 10 runs in all
         again, _ = p.attend(q)
         assert np.array_equal(first, again)
 
@@ -150,3 +150,24 @@ def test_workspace_shared_by_two_caches():
             q = rng.standard_normal((p.B, p.s.n_q_heads, p.s.d_head), dtype=np.float32).astype(np.float16)
             out, scale = p.attend(q, ws=ws)
             assert max_abs(out, p.ref.attention(q, scale)) <= ATOL, (p.s.cid, rep)
+
+
+def test_split_length_varied_on_one_input(monkeypatch):
+    """The same cache and queries attended with split lengths from the
+    shortest allowed (256 tokens, up to 5 splits here) to one split per
+    sequence: every result within 2e-3 of the oracle, and of each other."""
+    s = W.spec(2, batch=3, seq_len=1200, min_len=900)
+    k, v, lens = prefill_inputs(s, 0)
+    p = Pair(s, s.max_tokens(8))
+    p.append(k, v, lens)
+    q = np.random.default_rng(10).standard_normal((3, 32, 128), dtype=np.float32).astype(np.float16)
+    outs = []
+    for tokens in (256, 512, 1024, 1 << 20):
+        monkeypatch.setenv("KVQ_SPLIT_TOKENS", str(tokens))
+        out, scale = p.attend(q)
+        print(f"split length {tokens}: max-abs {max_abs(out, p.ref.attention(q, scale)):.3e}", flush=True)
+        assert max_abs(out, p.ref.attention(q, scale)) <= ATOL, tokens
+        outs.append(out)
+    monkeypatch.delenv("KVQ_SPLIT_TOKENS")
+    for o in outs[1:]:
+        assert max_abs(o, outs[0]) <= ATOL
