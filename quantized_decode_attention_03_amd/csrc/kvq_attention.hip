@@ -155,7 +155,8 @@ __device__ __forceinline__ int key_channel(int grp, int j, int p, int second) {
 //   [key meta: 128 words (channel axis) or 32 (token axis)][sparse 32 x 2 words]
 // Key codes and the value block are contiguous in global memory and move
 // with 1 KiB direct-to-LDS loads (64 lanes x 16 bytes); the metadata pieces
-// move together in one more load whose lanes gather 16-byte chunks.
+// follow with one load per array, each lane group gathering 16-byte chunks
+// into consecutive LDS.
 template <int KB, int VB, int KAXIS, int G, bool SPARSE>
 struct Geom {
   static constexpr int kRowK = 16 * KB;               // key code bytes per token
@@ -166,7 +167,7 @@ struct Geom {
   static constexpr int kSp = SPARSE ? 256 : 0;
   static constexpr int kMetaLanes = (kVm + kKm + kSp) / 16;
   static constexpr int kBytes = kK + kV + kVm + kKm + kSp;
-  static constexpr int kLoads = kK / 1024 + kV / 1024 + 1;   // DMA instructions per tile
+  static constexpr int kLoads = kK / 1024 + kV / 1024 + (SPARSE ? 3 : 2);  // DMA instructions per tile
   // the key-product B operand and zero-point operand (channel axis only)
   static constexpr int kWaveLds = KAXIS ? (4 * (2 * G + 1) * 4 * 16 + 4 * 4 * 4 * 4) : 0;
   // tile slots per wavefront: as many as fit the per-wavefront LDS budget
@@ -178,22 +179,31 @@ struct Geom {
   static_assert(kMetaLanes <= 64, "metadata fits one load");
 };
 
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16*lane
-// (gfx950 global_load_lds_dwordx4). Issued from inline assembly so that the
-// compiler neither waits on it at every LDS read nor keeps stale LDS values
-// across it; completion is awaited explicitly with wait_vm().
-// dma16: per-lane 64-bit address. dma16s: wave-uniform base in SGPRs plus a
-// per-lane 32-bit byte offset.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds_base)
-               : "memory", "m0");
+// Buffer resource (V#) over `bytes` bytes at `base`: a raw descriptor (stride
+// 0) whose loads read zeros, without touching memory, at any offset at or past
+// `bytes`. The four words are made wave-uniform (readfirstlane), each as a
+// 32-bit value, so they live in SGPRs.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  u32x4 r;
+  r.x = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) & 0xFFFFu;  // stride 0
+  r.z = (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes);                          // num_records
+  r.w = 0x00020000u;  // 32-bit data format, no swizzle, no index
+  return r;
 }
-__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+
+// 16 bytes per lane from a buffer (byte offset voff) straight into LDS at
+// lds_base + 16 * lane (gfx950 buffer_load_dwordx4 ... lds). Issued from
+// inline assembly so that the compiler neither waits on it at every LDS read
+// nor keeps stale LDS values across it; completion is awaited explicitly with
+// wait_vm(). The offset sits entirely in the VGPR operand (no SGPR or
+// immediate offset), which is what the range check covers.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(off), "s"(base), "s"(lds_base)
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
 template <int N>
@@ -329,41 +339,53 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   const int tq = (Q > ts0) ? min((Q - ts0 + kBlock - 1) / kBlock, ntiles) : 0;  // quantized tiles
   const int nw = (w < tq) ? (tq - w + 3) / 4 : 0;                               // of them, mine
 
-  // DMA sources of the next tile to issue. Key codes and value blocks: a
-  // wave-uniform base plus lane * 16 (+ 1 KiB steps); metadata: the lanes
-  // gather 16-byte pieces of three arrays through per-lane pointers. Each
-  // advances by 4 tiles per issue (the wavefront takes every 4th tile).
+  // Tile loads go through bounded descriptors over this (sequence, KV head)'s
+  // slice of each cache array, so an offset outside the slice reads zeros
+  // and never touches other memory. Byte offsets of the next tile to issue:
+  // key codes and value blocks, the tile's start plus lane * 16 (+ 1 KiB
+  // steps); metadata, each lane its 16-byte piece of one of the arrays (value
+  // scales, key scales, sparse entries; one load per array). Offsets advance
+  // by 4 tiles per issue (the wavefront takes every 4th tile).
   const int tw0 = ts0 + w * kBlock;
-  const uint8_t* kgs = c.k_codes + (bh * c.T + tw0) * (size_t)Gm::kRowK;
-  const uint8_t* vgs = c.v_codes + (bh * (c.T / kBlock) + tw0 / kBlock) * (size_t)Gm::kV;
-  const uint8_t* mgp;
-  uint32_t mstep;
-  if (lane < 8) {
-    mgp = reinterpret_cast<const uint8_t*>(c.v_meta + bh * c.T + tw0) + lane * 16;
+  const uint32_t Tu = (uint32_t)c.T;
+  const u32x4 rk = make_rsrc(c.k_codes + bh * c.T * (size_t)Gm::kRowK, Tu * Gm::kRowK);
+  const u32x4 rv = make_rsrc(c.v_codes + bh * (c.T / kBlock) * (size_t)Gm::kV, (Tu / kBlock) * Gm::kV);
+  const u32x4 rvm = make_rsrc(c.v_meta + bh * c.T, Tu * 4);
+  const u32x4 rkm = KAXIS ? make_rsrc(c.k_meta + bh * (c.T / kBlock) * kD, (Tu / kBlock) * kD * 4)
+                          : make_rsrc(c.k_meta + bh * c.T, Tu * 4);
+  const u32x4 rsp = SPARSE ? make_rsrc(c.k_sparse + bh * c.T * 2, Tu * 8) : rvm;
+  uint32_t koff = (uint32_t)tw0 * Gm::kRowK + lane * 16;
+  uint32_t voff = (uint32_t)(tw0 / kBlock) * Gm::kV + lane * 16;
+  // metadata lanes: 0..7 value scales, then key scales, then sparse entries
+  const int mkind = lane < 8 ? 0 : (lane < 8 + Gm::kKm / 16 ? 1 : 2);
+  uint32_t moff, mstep;
+  if (mkind == 0) {
+    moff = (uint32_t)tw0 * 4 + lane * 16;
     mstep = 4 * kBlock * 4;
-  } else if (lane < 8 + Gm::kKm / 16) {
-    const uint32_t* km = KAXIS ? c.k_meta + (bh * (c.T / kBlock) + tw0 / kBlock) * kD
-                               : c.k_meta + bh * c.T + tw0;
-    mgp = reinterpret_cast<const uint8_t*>(km) + (lane - 8) * 16;
+  } else if (mkind == 1) {
+    moff = (KAXIS ? (uint32_t)(tw0 / kBlock) * kD * 4 : (uint32_t)tw0 * 4) + (lane - 8) * 16;
     mstep = KAXIS ? 4 * kD * 4 : 4 * kBlock * 4;
   } else {
-    const int sl = min(lane - 8 - Gm::kKm / 16, 15);
-    mgp = reinterpret_cast<const uint8_t*>(c.k_sparse + (bh * c.T + tw0) * 2) + sl * 16;
+    moff = (uint32_t)tw0 * 8 + (uint32_t)(lane - 8 - Gm::kKm / 16) * 16;
     mstep = 4 * kBlock * 8;
   }
-  const uint32_t loff = lane * 16;
 
   // DMA of the next tile of this wavefront into slot `slot`.
   auto issue = [&](int slot) {
     const uint32_t lb = wbase_lds + slot * Gm::kBytes;
 #pragma unroll
-    for (int x = 0; x < Gm::kK / 1024; ++x) dma16s(kgs, loff + x * 1024, lb + x * 1024);
+    for (int x = 0; x < Gm::kK / 1024; ++x) dma16(rk, koff + x * 1024, lb + x * 1024);
 #pragma unroll
-    for (int x = 0; x < Gm::kV / 1024; ++x) dma16s(vgs, loff + x * 1024, lb + Gm::kK + x * 1024);
-    if (lane < Gm::kMetaLanes) dma16(mgp, lb + Gm::kK + Gm::kV);
-    kgs += 4 * Gm::kK;
-    vgs += 4 * Gm::kV;
-    mgp += mstep;
+    for (int x = 0; x < Gm::kV / 1024; ++x) dma16(rv, voff + x * 1024, lb + Gm::kK + x * 1024);
+    const uint32_t lbm = lb + Gm::kK + Gm::kV;
+    if (mkind == 0) dma16(rvm, moff, lbm);
+    if (mkind == 1) dma16(rkm, moff, lbm);
+    if constexpr (SPARSE) {
+      if (mkind == 2 && lane < Gm::kMetaLanes) dma16(rsp, moff, lbm);
+    }
+    koff += 4 * Gm::kK;
+    voff += 4 * Gm::kV;
+    moff += mstep;
   };
 
   float m_ref = -INFINITY, l_run = 0.f;

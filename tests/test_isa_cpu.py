@@ -1,6 +1,12 @@
 """Checks on the generated gfx950 code of the HIP kernels (no GPU needed:
 hipcc cross-compiles to assembly here).
 
+* The attention kernel's tile loads go straight to LDS through buffer
+  descriptors with a range check: each is a `buffer_load_dwordx4 ... offen
+  lds` whose whole offset is in the VGPR operand (SGPR offset 0, no immediate),
+  the part the hardware range-checks, so an offset past a descriptor's size
+  reads zeros instead of faulting. No unchecked pointer form
+  (`global_load_lds_*`) is left in any kernel.
 * M0 holds the LDS address of the direct-to-LDS tile loads, which are issued
   from inline assembly. The compiler does not treat M0 as clobbered by inline
   assembly, so the kernels are correct only while no compiler-generated
@@ -59,8 +65,7 @@ def test_m0_only_inside_inline_asm(asm):
 def test_dma_loads_only_in_inline_asm(asm):
     # the loads whose LDS address comes from M0 are exactly the inline-asm ones
     text = asm["kvq_attention.hip"]
-    n_asm = text.count("global_load_lds_dwordx4")
-    assert n_asm > 0
+    assert len(re.findall(r"buffer_load_dwordx4 .*\blds\b", text)) > 0
     inside = False
     for line in text.split("\n"):
         t = line.strip()
@@ -68,8 +73,20 @@ def test_dma_loads_only_in_inline_asm(asm):
             inside = True
         elif t.startswith(";;#ASMEND"):
             inside = False
-        elif "global_load_lds" in t and not t.startswith(";"):
+        elif re.search(r"_load_.*\blds\b", t) and not t.startswith(";"):
             assert inside, t
+
+
+def test_dma_loads_are_range_checked(asm):
+    # every LDS load is a raw buffer load with the whole offset in the VGPR
+    # (SGPR offset 0, no immediate offset); no unchecked pointer form remains
+    for src, text in asm.items():
+        assert "global_load_lds" not in text, f"{src}: unchecked pointer DMA"
+        for line in text.split("\n"):
+            t = line.strip()
+            if t.startswith(";") or not re.search(r"_load_.*\blds\b", t):
+                continue
+            assert re.fullmatch(r"buffer_load_dwordx4 v\d+, s\[\d+:\d+\], 0 offen lds", t), (src, t)
 
 
 def _kernel_meta(text):
