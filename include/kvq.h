@@ -34,14 +34,19 @@
  *                      s16 = smallest fp16 >= s32 (round toward +inf)
  *   else (constant):   s16 = |x_min| if x_min != 0, else 1.0
  *   s  = (float)s16
- *   z  = (float)q_min - rint(x_min / s), clamped to [-2048, 2048]; z16 = fp16(z)
+ *   r  = rint(x_min / s)
+ *   if |r| > 2048 + q_min (a group far from zero compared with its spread):
+ *                      s16 = smallest fp16 >= |x_min| / (float)(2048 + q_min),
+ *                      s = (float)s16, r = rint(x_min / s)
+ *   z  = (float)q_min - r;  z16 = fp16(z)
+ *   (|r| <= 2048 + q_min keeps z and z - q_min = -r exact fp16 integers)
  *   q_i = clamp(rint(x_i / s) + z, q_min, q_max)       (rint: half to even)
  *   stored code u_i = q_i - q_min  (unsigned, b bits)
  *   x_hat_i = s * (q_i - z)   (exact in fp32)
  * Divisions are true IEEE divisions, never multiplication by a reciprocal.
- * Rounding the scale up keeps every in-range element within s/2 of its
- * reconstruction, the bound the "Integer quantization in one screen" section
- * states.
+ * Rounding the scale up, and widening it for far-off groups, keeps every
+ * element within s/2 of its reconstruction at the stored scale, the bound the
+ * "Integer quantization in one screen" section states.
  *
  * Token state of one sequence (per KV head, identical for all heads)
  *   L  = tokens held (device seq_len[b]; host copy len_host[b]).

@@ -19,8 +19,15 @@ Readings where the page is silent (each is also listed in the design notes):
   * q is clamped to [q_min, q_max] (needed at half-way ties).
   * A constant group (x_max == x_min) would divide by zero; it takes scale =
     |x_min| (or 1 when x_min == 0), which reconstructs every element exactly.
-  * The zero-point is stored as fp16 and clamped to [-2048, 2048], the range in
-    which every integer is an fp16.
+  * The zero-point is stored as fp16, which holds every integer in
+    [-2048, 2048] exactly; codes are stored unsigned (q - q_min), so the zero
+    point in those units, z - q_min = -round(x_min / scale), must be an exact
+    fp16 integer too. Both hold while |round(x_min / scale)| <= 2048 + q_min.
+    A group lying far from zero compared with its spread breaks that; such a
+    group instead takes the smallest fp16 scale >= |x_min| / (2048 + q_min),
+    which brings round(x_min / scale) back inside. The codes then still use at
+    most the q_max - q_min steps of the range, so every element stays within
+    scale/2 of its reconstruction at the stored (wider) scale.
   * int2 uses [-2, 1] (two's complement, the four levels of [P1-kivi]).
 
 Symmetric groups ([P2-int] "Symmetric vs asymmetric") force the zero point to
@@ -33,7 +40,7 @@ import numpy as np
 F16 = np.float16
 F32 = np.float32
 
-ZERO_CLAMP = 2048.0
+F16_INT_LIMIT = 2048  # every integer of magnitude <= 2048 is an exact fp16
 
 
 def qrange(bits):
@@ -82,8 +89,16 @@ def group_scale_zero(xmin, xmax, bits):
         s_const = np.where(xmin != 0, np.abs(xmin), F32(1.0)).astype(F16)
         s16 = np.where(const, s_const, s16)
         s = s16.astype(F32)
-        z = F32(qmin) - np.rint(xmin / s)                # zero_point, fp32
-    z = np.clip(z, F32(-ZERO_CLAMP), F32(ZERO_CLAMP))
+        r = np.rint(xmin / s)                            # round(x_min / scale)
+        # zero points that fp16 would not hold exactly: widen the scale instead
+        lim = F32(F16_INT_LIMIT + qmin)
+        wide = np.abs(r) > lim
+        if np.any(wide):
+            s16 = np.where(wide, f32_to_f16_up(np.abs(xmin) / lim), s16)
+            s = s16.astype(F32)
+            r = np.rint(xmin / s)
+        z = F32(qmin) - r                                # zero_point, fp32
+    assert np.all(np.abs(r) <= lim) and np.all(np.abs(z) <= F16_INT_LIMIT)
     return s16, z.astype(F16)
 
 

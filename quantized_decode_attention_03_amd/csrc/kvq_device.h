@@ -50,8 +50,19 @@ __device__ __forceinline__ GroupQ group_params(float xmin, float xmax, int bits)
   }
   GroupQ g;
   g.s = h2f(s16);
-  float z = (float)qmin_of(bits) - __builtin_rintf(xmin / g.s);
-  z = __builtin_fminf(__builtin_fmaxf(z, -2048.0f), 2048.0f);
+  float r = __builtin_rintf(xmin / g.s);
+  constexpr float kLim0 = 2048.0f;  // every integer up to 2048 is an exact fp16
+  const float lim = kLim0 + (float)qmin_of(bits);
+  if (__builtin_fabsf(r) > lim) {
+    // a group far from zero compared with its spread: the zero point z, or
+    // z - q_min in stored-code units, would not be an exact fp16 integer, so
+    // the scale widens until |round(x_min / s)| <= 2048 + q_min (the codes
+    // still span at most q_max - q_min steps, keeping the scale/2 bound)
+    s16 = f2h_up(__builtin_fabsf(xmin) / lim);
+    g.s = h2f(s16);
+    r = __builtin_rintf(xmin / g.s);
+  }
+  const float z = (float)qmin_of(bits) - r;
   g.z = z;
   g.meta = (uint32_t)s16 | ((uint32_t)f2h_rne(z) << 16);
   return g;

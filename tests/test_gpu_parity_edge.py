@@ -6,7 +6,10 @@
 * inputs of fp16-subnormal size (subnormal scales);
 * value vectors of large magnitude (the largest value scales, which drive the
   attention kernel's value-scale exponent furthest);
-* a zero query (uniform softmax weights).
+* a zero query (uniform softmax weights);
+* groups far from zero compared with their spread (the widened scale): a key
+  channel near +60 with a small spread (channel-axis groups), key and value
+  vectors near -40 and +25 (token-axis groups).
 Codes, metadata and residual keys byte-equal; attention within 2e-3, or within
 2e-3 relative to the largest |value| where the values themselves are large."""
 import numpy as np
@@ -89,4 +92,15 @@ def test_zero_query(cid):
         s, lens = W.spec(cid, batch=2, seq_len=200, min_len=70), [200, 70]
     k, v, q = _inputs(s, lens, 14)
     q[:] = 0
+    _run(s, k, v, lens, q)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 4])
+def test_offset_groups(cid):
+    s, lens = _shape(cid, N_TOK[cid])
+    k, v, q = _inputs(s, lens, 15)
+    f = np.float32
+    k[:, :, 7] = (k[:, :, 7].astype(f) * f(0.02) + f(60)).astype(F16)
+    k[20:30] = (k[20:30].astype(f) * f(0.001) - f(40)).astype(F16)
+    v[40:50] = (v[40:50].astype(f) * f(0.001) + f(25)).astype(F16)
     _run(s, k, v, lens, q)

@@ -19,7 +19,7 @@ def _cases():
         return json.load(f)["cases"]
 
 
-@pytest.mark.parametrize("case", _cases(), ids=lambda c: f"int{c['bits']}")
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: f"int{c['bits']}-{c['x'][0]}")
 def test_hand_cases(case):
     x = np.array(case["x"], np.float16)[None]
     q, s, z = quant.quantize_groups(x, case["bits"])
@@ -68,16 +68,24 @@ def test_error_bound(bits, n):
     x[::7, 3] *= 20
     x[::11] *= 1e-3
     x[::13] += 5
+    # groups far from zero compared with their spread (widened scale)
+    x[1::17] = x[1::17] * 1e-2 + 300
+    x[2::19] = x[2::19] * 1e-3 - 40
     x = x.astype(np.float16)
     q, s, z = quant.quantize_groups(x, bits)
-    # the bound holds wherever the zero-point is not clamped (|z| < 2048);
-    # groups offset far from zero relative to their spread fall outside
-    ok = np.abs(z.astype(np.float32)) < 2048
-    assert ok.mean() > 0.97
+    xf = x.astype(np.float32)
+    qmin, qmax = quant.qrange(bits)
+    s_formula = quant.f32_to_f16_up((xf.max(1) - xf.min(1)) / np.float32(qmax - qmin))
+    widened = s.astype(np.float32) > s_formula.astype(np.float32)
+    assert widened.sum() >= 100
+    # every zero point is an integer fp16 holds exactly
+    zf = z.astype(np.float64)
+    assert np.all(np.abs(zf) <= 2048) and np.all(zf == np.rint(zf))
     xh = quant.dequantize(q, s[:, None], z[:, None]).astype(np.float64)
-    err = np.abs(x.astype(np.float64) - xh)[ok]
-    bound = s.astype(np.float64)[ok, None] * (0.5 + 2.0 ** -12)
+    err = np.abs(x.astype(np.float64) - xh)
+    bound = s.astype(np.float64)[:, None] * (0.5 + 2.0 ** -12)
     assert np.all(err <= bound)
+    assert np.all(err[widened] <= bound[widened])
     # the bound is attained (up to the slack) on some element: it is tight
     assert np.max(err / bound) > 0.9
 
@@ -138,13 +146,26 @@ def test_constant_groups_exact(bits):
     assert np.array_equal(xh, x.astype(np.float32))
 
 
-def test_zero_point_clamp():
-    """A group far from zero relative to its spread: z saturates at -2048 and
-    every code then sits at q_max (the reading for this out-of-domain case)."""
-    x = np.float16([[1000.0, 1000.5, 1001.0, 1000.25]])
-    q, s, z = quant.quantize_groups(x, 8)
-    assert float(z[0]) == -2048.0
-    assert np.all(q == 127)
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_offset_groups_keep_the_bound(bits):
+    """Groups far from zero compared with their spread would need a zero point
+    fp16 cannot hold; the widened scale keeps |z| <= 2048, the minimum on
+    q_min, no code past q_max, and the scale/2 bound. Offsets of both signs
+    and sizes up to the fp16 range."""
+    qmin, qmax = quant.qrange(bits)
+    rng = np.random.default_rng(40 + bits)
+    off = np.concatenate([10.0 ** rng.uniform(1, 4.5, 500), -(10.0 ** rng.uniform(1, 4.5, 500))])
+    x = (off[:, None] + rng.standard_normal((1000, 32)) * np.abs(off[:, None]) * 1e-3)
+    x = np.clip(x, -65504, 65504).astype(np.float16)
+    q, s, z = quant.quantize_groups(x, bits)
+    assert np.all(np.abs(z.astype(np.float64)) <= 2048)
+    # the zero point in stored-code units (z - q_min) is an exact fp16 integer too
+    assert np.all(np.abs(z.astype(np.float64) - qmin) <= 2048 + qmin)
+    xf = x.astype(np.float64)
+    assert np.all(q[np.arange(1000), xf.argmin(1)] == qmin)
+    assert np.all(q <= qmax)
+    xh = quant.dequantize(q, s[:, None], z[:, None]).astype(np.float64)
+    assert np.all(np.abs(xf - xh) <= s.astype(np.float64)[:, None] * (0.5 + 2.0 ** -12))
 
 
 def test_symmetric_data_int8_zero():
