@@ -176,15 +176,18 @@ typedef struct kvq_sizes {
   uint64_t total_bytes;    /* sum of every array above                      */
 } kvq_sizes;
 
-/* Fills *out_host. KVQ_EINVAL / KVQ_EUNSUPPORTED on a bad configuration or
- * size. Pure host function. */
+/* Fills *out_host. max_tokens must be a positive multiple of 32;
+ * KVQ_EINVAL on a bad configuration, size or null pointer, KVQ_EUNSUPPORTED
+ * past 2^24 tokens per sequence (the capacity a kvq_cache can describe).
+ * Pure host function. */
 kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch,
-                           int32_t max_tokens, kvq_sizes* out_host);
+                           int64_t max_tokens, kvq_sizes* out_host);
 
 /* Bytes of device workspace kvq_decode_attention needs for this shape
- * (split-K partial results). 0 on a bad configuration. Pure host function. */
+ * (split-K partial results). 0 on a bad configuration or size (the rules of
+ * kvq_cache_sizes). Pure host function. */
 size_t kvq_workspace_bytes(const kvq_config* cfg, int32_t batch,
-                           int32_t max_tokens);
+                           int64_t max_tokens);
 
 /* Quantize-on-append. Appends n_new_host[b] tokens of keys and values to
  * sequence b, quantizing per the group arithmetic above: values per token;

@@ -48,6 +48,25 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def _check(t, name, dtype, shape=None, device=None):
+    """Raise ValueError unless t is a contiguous device tensor of the given
+    dtype (and shape and device); the kernels read exactly that many elements
+    through the raw pointer."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, the cache is on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def _stream(stream):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -75,6 +94,9 @@ class KVCache:
         import torch
         self.cfg, self.batch, self.max_tokens = cfg, batch, max_tokens
         sz = kvq_cache_sizes(cfg, batch, max_tokens)
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.sizes = sz
 
         def buf(n):
@@ -110,9 +132,27 @@ class KVCache:
 
 
 def kvq_append(cache, k_new, v_new, cu_new, n_new, stream=None):
-    """k_new, v_new: fp16 device tensors [N, H, D]; cu_new: int32 device
-    tensor [B+1]; n_new: host sequence of B ints."""
-    n = (ctypes.c_int32 * cache.batch)(*[int(x) for x in n_new])
+    """k_new, v_new: fp16 device tensors [N, H, D], N = sum(n_new), the new
+    tokens of all sequences back to back; cu_new: int32 device tensor [B+1]
+    of their prefix offsets (None: built here from n_new); n_new: host
+    sequence of B ints."""
+    import torch
+    n_list = [int(x) for x in n_new]
+    if len(n_list) != cache.batch:
+        raise ValueError(f"n_new: {len(n_list)} counts for a batch of {cache.batch}")
+    if any(x < 0 for x in n_list):
+        raise ValueError("n_new: negative count")
+    cfg, dev = cache.cfg, cache.device
+    rows = (sum(n_list), cfg.n_kv_heads, cfg.d_head)
+    _check(k_new, "k_new", torch.float16, rows, dev)
+    _check(v_new, "v_new", torch.float16, rows, dev)
+    if cu_new is None:
+        cu = [0]
+        for x in n_list:
+            cu.append(cu[-1] + x)
+        cu_new = torch.tensor(cu, dtype=torch.int32, device=dev)
+    _check(cu_new, "cu_new", torch.int32, (cache.batch + 1,), dev)
+    n = (ctypes.c_int32 * cache.batch)(*n_list)
     N.check(N.lib().kvq_append(ctypes.byref(cache._cfg), ctypes.byref(cache._c), _ptr(k_new),
                                _ptr(v_new),
                                ctypes.cast(ctypes.c_void_p(cu_new.data_ptr()),
@@ -121,8 +161,13 @@ def kvq_append(cache, k_new, v_new, cu_new, n_new, stream=None):
 
 
 def kvq_decode_attention(cache, q, out, softmax_scale, ws, stream=None):
-    """q: fp16 [B, Hq, D]; out: fp32 [B, Hq, D]; ws: device buffer of at least
-    kvq_workspace_bytes bytes."""
+    """q: fp16 [B, Hq, D]; out: fp32 [B, Hq, D]; ws: contiguous device
+    buffer of at least kvq_workspace_bytes bytes (any dtype)."""
+    import torch
+    cfg, dev = cache.cfg, cache.device
+    _check(q, "q", torch.float16, (cache.batch, cfg.n_q_heads, cfg.d_head), dev)
+    _check(out, "out", torch.float32, (cache.batch, cfg.n_q_heads, cfg.d_head), dev)
+    _check(ws, "ws", ws.dtype if isinstance(ws, torch.Tensor) else None, None, dev)
     N.check(N.lib().kvq_decode_attention(ctypes.byref(cache._cfg), ctypes.byref(cache._c),
                                          _ptr(q), _ptr(out), ctypes.c_float(softmax_scale),
                                          _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()),
@@ -131,5 +176,10 @@ def kvq_decode_attention(cache, q, out, softmax_scale, ws, stream=None):
 
 def kvq_dequantize(cache, k_out, v_out, stream=None):
     """k_out, v_out: fp16 device tensors [B, T, H, D]."""
+    import torch
+    cfg, dev = cache.cfg, cache.device
+    shape = (cache.batch, cache.max_tokens, cfg.n_kv_heads, cfg.d_head)
+    _check(k_out, "k_out", torch.float16, shape, dev)
+    _check(v_out, "v_out", torch.float16, shape, dev)
     N.check(N.lib().kvq_dequantize(ctypes.byref(cache._cfg), ctypes.byref(cache._c), _ptr(k_out),
                                    _ptr(v_out), _stream(stream)), "kvq_dequantize")

@@ -55,9 +55,10 @@ def lib():
                                "`python -m quantized_decode_attention_03_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         cp, vp, i32, i32p = ctypes.POINTER, ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)
-        L.kvq_cache_sizes.argtypes = [cp(kvq_config), i32, i32, cp(kvq_sizes)]
+        i64 = ctypes.c_int64
+        L.kvq_cache_sizes.argtypes = [cp(kvq_config), i32, i64, cp(kvq_sizes)]
         L.kvq_cache_sizes.restype = ctypes.c_int
-        L.kvq_workspace_bytes.argtypes = [cp(kvq_config), i32, i32]
+        L.kvq_workspace_bytes.argtypes = [cp(kvq_config), i32, i64]
         L.kvq_workspace_bytes.restype = ctypes.c_size_t
         L.kvq_append.argtypes = [cp(kvq_config), cp(kvq_cache), vp, vp, i32p, i32p, vp]
         L.kvq_append.restype = ctypes.c_int

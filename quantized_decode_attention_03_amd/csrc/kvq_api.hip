@@ -130,7 +130,7 @@ kvq_status check_config(const kvq_config* cfg) {
   return KVQ_OK;
 }
 
-kvq_status check_shape(int32_t batch, int32_t max_tokens) {
+kvq_status check_shape(int32_t batch, int64_t max_tokens) {
   if (batch < 1 || max_tokens < kBlock || max_tokens % kBlock != 0) return KVQ_EINVAL;
   if (max_tokens > (1 << 24)) return KVQ_EUNSUPPORTED;
   return KVQ_OK;
@@ -189,7 +189,7 @@ const char* kvq_status_string(kvq_status s) {
   return "unknown status";
 }
 
-kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch, int32_t max_tokens,
+kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch, int64_t max_tokens,
                            kvq_sizes* out) {
   kvq_status s = check_config(cfg);
   if (s != KVQ_OK) return s;
@@ -214,9 +214,9 @@ kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch, int32_t max_tok
   return KVQ_OK;
 }
 
-size_t kvq_workspace_bytes(const kvq_config* cfg, int32_t batch, int32_t max_tokens) {
+size_t kvq_workspace_bytes(const kvq_config* cfg, int32_t batch, int64_t max_tokens) {
   if (check_config(cfg) != KVQ_OK || check_shape(batch, max_tokens) != KVQ_OK) return 0;
-  return (size_t)batch * cfg->n_q_heads * max_splits_for(max_tokens) * kPartialFloats * sizeof(float);
+  return (size_t)batch * cfg->n_q_heads * max_splits_for((int)max_tokens) * kPartialFloats * sizeof(float);
 }
 
 kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new, const void* v_new,
@@ -227,10 +227,12 @@ kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new
   if (!cu_new_dev || !n_new_host) return KVQ_EINVAL;
   int64_t total = 0;
   int max_tok_blocks = 0, max_flush_blocks = 0;
+  bool one_each = true;  // a decode step: one new token for every sequence
   const int R = cfg->k_residual_tokens;
   for (int b = 0; b < cache->batch; ++b) {
     const int n = n_new_host[b];
     if (n < 0) return KVQ_EINVAL;
+    one_each = one_each && n == 1;
     const int L = cache->len_host[b];
     if ((int64_t)L + n > cache->max_tokens) return KVQ_ECAPACITY;
     total += n;
@@ -243,15 +245,20 @@ kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new
     }
   }
   if (total == 0) return KVQ_OK;
+  if (total > INT32_MAX) return KVQ_EINVAL;
   if (!k_new || !v_new || !aligned(k_new) || !aligned(v_new)) return KVQ_EINVAL;
   const CacheView v = view_of(cfg, cache);
-  const AppendInputs in{(const uint16_t*)k_new, (const uint16_t*)v_new, cu_new_dev};
+  const AppendInputs in{(const uint16_t*)k_new, (const uint16_t*)v_new, cu_new_dev, (int)total};
   hipStream_t st = (hipStream_t)stream;
   if (max_flush_blocks > 0) {
     if ((s = after_launch(launch_flush_keys(v, in, max_flush_blocks, st), st)) != KVQ_OK) return s;
   }
-  if ((s = after_launch(launch_append_tokens(v, in, max_tok_blocks, st), st)) != KVQ_OK) return s;
-  if ((s = after_launch(launch_update_lengths(v, cu_new_dev, st), st)) != KVQ_OK) return s;
+  if (one_each) {
+    if ((s = after_launch(launch_append_decode(v, in, st), st)) != KVQ_OK) return s;
+  } else {
+    if ((s = after_launch(launch_append_tokens(v, in, max_tok_blocks, st), st)) != KVQ_OK) return s;
+    if ((s = after_launch(launch_update_lengths(v, in, st), st)) != KVQ_OK) return s;
+  }
   for (int b = 0; b < cache->batch; ++b) cache->len_host[b] += n_new_host[b];
   return KVQ_OK;
 }

@@ -11,6 +11,10 @@
 // low-bit numbers actually cost"; the per-token/per-channel choice: "KV Cache
 // Quantization — 8-bit and 4-bit", "Why keys and values want different
 // treatment".)
+//
+// Counts read from the device (lengths, new-token offsets) are clamped to the
+// cache capacity and to the rows of the packed input, so inconsistent
+// arguments give wrong contents but never an access outside the buffers.
 #include "kvq_device.h"
 
 namespace kvq {
@@ -36,6 +40,20 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
   return v;
 }
 
+// Sequence b's state before the append: L tokens held, its new tokens are
+// rows row0 .. row0 + n - 1 of the packed input. Clamped: 0 <= L <= T,
+// 0 <= row0 <= rows, 0 <= n <= min(T - L, rows - row0).
+struct SeqNew {
+  int L, row0, n;
+};
+__device__ __forceinline__ SeqNew seq_new(const CacheView& c, const AppendInputs& in, int b) {
+  SeqNew s;
+  s.L = min(max(c.seq_len[b], 0), c.T);
+  s.row0 = min(max(in.cu_new[b], 0), in.rows);
+  s.n = min(max(in.cu_new[b + 1] - s.row0, 0), min(in.rows - s.row0, c.T - s.L));
+  return s;
+}
+
 // Per-channel key flush: one workgroup per (32-token block of the window,
 // KV head, sequence). The window is tokens [Q, Q2) with Q = L - L mod R and
 // Q2 = L2 - L2 mod R; tokens below L come from the residual, the rest from
@@ -43,19 +61,18 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
 __global__ __launch_bounds__(256) void flush_keys_kernel(CacheView c, AppendInputs in) {
   const int b = blockIdx.z, h = blockIdx.y, blk = blockIdx.x;
   const int tid = threadIdx.x;
-  const int L = c.seq_len[b];
-  const int row0 = in.cu_new[b];
-  const int n = in.cu_new[b + 1] - row0;
-  const int R = c.R;
-  const int Q = L - L % R, L2 = L + n, Q2 = L2 - L2 % R;
+  const SeqNew sn = seq_new(c, in, b);
+  const int L = sn.L, row0 = sn.row0, R = c.R;
+  const int Q = L - L % R, L2 = L + sn.n, Q2 = L2 - L2 % R;
   const int t0 = Q + blk * kBlock;
   if (t0 + kBlock > Q2) return;
   const size_t bh = (size_t)b * c.H + h;
 
   __shared__ uint16_t xs[kBlock][kD];
   __shared__ uint8_t codes[kBlock][kD];
+  __shared__ float part[2][2][kD];  // [min, max][token half][channel]
 
-  {  // stage the 32 x 128 fp16 block
+  {  // stage the 32 x 128 fp16 block: 8 threads per 256-byte token row
     const int tau = tid >> 3, c0 = (tid & 7) * 16;
     const int t = t0 + tau;
     const uint16_t* src = (t < L)
@@ -94,22 +111,31 @@ __global__ __launch_bounds__(256) void flush_keys_kernel(CacheView c, AppendInpu
     __syncthreads();
   }
 
-  if (tid < kD) {  // one thread per channel group (32 tokens)
-    const int ch = tid;
-    float mn = h2f(xs[0][ch]), mx = mn;
-    for (int tau = 1; tau < kBlock; ++tau) {
-      const float v = h2f(xs[tau][ch]);
-      mn = __builtin_fminf(mn, v);
-      mx = __builtin_fmaxf(mx, v);
-    }
-    const GroupQ g = group_params(mn, mx, c.kbits);
-    c.k_meta[(bh * (c.T / kBlock) + t0 / kBlock) * kD + ch] = g.meta;
-    for (int tau = 0; tau < kBlock; ++tau)
-      codes[tau][ch] = (uint8_t)quant_code(h2f(xs[tau][ch]), g, c.kbits);
+  // two threads per channel group, 16 tokens each: partial extremes, then
+  // the group's scale and zero point (identical in both), then the codes
+  const int ch = tid & (kD - 1), half = tid >> 7;
+  const int tb = 16 * half;
+  float xv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) xv[i] = h2f(xs[tb + i][ch]);
+  float mn = xv[0], mx = xv[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    mn = __builtin_fminf(mn, xv[i]);
+    mx = __builtin_fmaxf(mx, xv[i]);
   }
+  part[0][half][ch] = mn;
+  part[1][half][ch] = mx;
+  __syncthreads();
+  mn = __builtin_fminf(part[0][0][ch], part[0][1][ch]);
+  mx = __builtin_fmaxf(part[1][0][ch], part[1][1][ch]);
+  const GroupQ g = group_params(mn, mx, c.kbits);
+  if (half == 0) c.k_meta[(bh * (c.T / kBlock) + t0 / kBlock) * kD + ch] = g.meta;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) codes[tb + i][ch] = (uint8_t)quant_code(xv[i], g, c.kbits);
   __syncthreads();
 
-  // pack token rows along channels
+  // pack token rows along channels (consecutive threads, consecutive words)
   const int kb = c.kbits, per = 32 / kb, row_words = 4 * kb;
   for (int i = tid; i < kBlock * row_words; i += 256) {
     const int tau = i / row_words, wd = i % row_words;
@@ -126,9 +152,8 @@ __global__ __launch_bounds__(256) void flush_keys_kernel(CacheView c, AppendInpu
 __global__ __launch_bounds__(256) void append_tokens_kernel(CacheView c, AppendInputs in) {
   const int b = blockIdx.z, h = blockIdx.y;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int L = c.seq_len[b];
-  const int row0 = in.cu_new[b];
-  const int n = in.cu_new[b + 1] - row0;
+  const SeqNew sn = seq_new(c, in, b);
+  const int L = sn.L, row0 = sn.row0, n = sn.n;
   if (n <= 0) return;
   const int L2 = L + n;
   const int j = L / kBlock + blockIdx.x;
@@ -199,9 +224,73 @@ __global__ __launch_bounds__(256) void append_tokens_kernel(CacheView c, AppendI
   }
 }
 
-__global__ void update_lengths_kernel(int32_t* seq_len, const int32_t* cu_new, int B) {
+// Decode-step append: one new token for every sequence. One workgroup per
+// sequence takes all its KV heads (a wavefront per head at a time), so it
+// alone reads and then advances seq_len[b]: no separate length update. Same
+// arithmetic and layout as append_tokens_kernel; the channel-axis flush of a
+// window this token fills runs before it (flush_keys_kernel).
+__global__ __launch_bounds__(256) void append_decode_kernel(CacheView c, AppendInputs in) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const SeqNew sn = seq_new(c, in, b);
+  if (sn.n < 1) return;  // a full sequence keeps its length
+  const int t = sn.L, L2 = sn.L + 1;
+  const bool ktok = c.kaxis == 0;
+  const int Q2 = ktok ? L2 : L2 - L2 % c.R;
+  const int j = t / kBlock, tau = t % kBlock;
+  for (int h = w; h < c.H; h += 4) {
+    const size_t bh = (size_t)b * c.H + h;
+    const size_t src = ((size_t)sn.row0 * c.H + h) * kD;
+    const uint32_t pr = reinterpret_cast<const uint32_t*>(in.v_new + src)[lane];
+    const uint32_t pk = reinterpret_cast<const uint32_t*>(in.k_new + src)[lane];
+    {  // value codes of channels 2 lane and 2 lane + 1 into their records
+      const float f0 = h2f((uint16_t)(pr & 0xFFFFu)), f1 = h2f((uint16_t)(pr >> 16));
+      const float mn = wave_min(__builtin_fminf(f0, f1)), mx = wave_max(__builtin_fmaxf(f0, f1));
+      const GroupQ g = group_params(mn, mx, c.vbits);
+      const uint32_t u0 = quant_code(f0, g, c.vbits), u1 = quant_code(f1, g, c.vbits);
+      if (lane == 0) c.v_meta[bh * c.T + t] = g.meta;
+      const int vb = c.vbits, per = 32 / vb, wd = tau / per, f = tau % per;
+      // fields of earlier tokens in the word are kept, later ones are zero
+      const uint32_t keep = (1u << (f * vb)) - 1u;
+      uint32_t* rec = reinterpret_cast<uint32_t*>(c.v_codes + (bh * (c.T / kBlock) + j) * (size_t)(kD * 4 * vb));
+      uint32_t* p0 = rec + (2 * lane) * vb + wd;
+      uint32_t* p1 = rec + (2 * lane + 1) * vb + wd;
+      const uint32_t o0 = f ? *p0 : 0u, o1 = f ? *p1 : 0u;
+      *p0 = (o0 & keep) | (u0 << (f * vb));
+      *p1 = (o1 & keep) | (u1 << (f * vb));
+    }
+    if (ktok) {  // the token's key row, channels packed low bits first
+      const float f0 = h2f((uint16_t)(pk & 0xFFFFu)), f1 = h2f((uint16_t)(pk >> 16));
+      const float mn = wave_min(__builtin_fminf(f0, f1)), mx = wave_max(__builtin_fmaxf(f0, f1));
+      const GroupQ g = group_params(mn, mx, c.kbits);
+      const uint32_t u0 = quant_code(f0, g, c.kbits), u1 = quant_code(f1, g, c.kbits);
+      if (lane == 0) c.k_meta[bh * c.T + t] = g.meta;
+      uint8_t* row = c.k_codes + (bh * c.T + t) * (size_t)(16 * c.kbits);
+      if (c.kbits == 8) {
+        reinterpret_cast<uint16_t*>(row)[lane] = (uint16_t)(u0 | (u1 << 8));
+      } else if (c.kbits == 4) {
+        row[lane] = (uint8_t)(u0 | (u1 << 4));
+      } else {  // byte m holds channels 4m .. 4m+3: lanes 2m and 2m + 1
+        const uint32_t v = u0 | (u1 << 2);
+        const uint32_t o = (uint32_t)__shfl_xor((int)v, 1, 64);
+        if ((lane & 1) == 0) row[lane >> 1] = (uint8_t)(v | (o << 4));
+      }
+    } else if (t >= Q2) {
+      reinterpret_cast<uint32_t*>(c.k_resid + (bh * c.R + (t - Q2)) * kD)[lane] = pk;
+    }
+  }
+  __syncthreads();  // every wavefront has read the old length
+  if (tid == 0) c.seq_len[b] = L2;
+}
+
+// Length update after append_tokens_kernel: one thread per sequence, the same
+// clamped count the append kernels used.
+__global__ void update_lengths_kernel(CacheView c, AppendInputs in) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b < B) seq_len[b] += cu_new[b + 1] - cu_new[b];
+  if (b < c.B) {
+    const SeqNew sn = seq_new(c, in, b);
+    c.seq_len[b] = sn.L + sn.n;
+  }
 }
 
 }  // namespace
@@ -220,9 +309,13 @@ hipError_t launch_append_tokens(const CacheView& c, const AppendInputs& in, int 
   return hipGetLastError();
 }
 
-hipError_t launch_update_lengths(const CacheView& c, const int32_t* cu_new, hipStream_t st) {
-  hipLaunchKernelGGL(update_lengths_kernel, dim3((c.B + 255) / 256), dim3(256), 0, st,
-                     c.seq_len, cu_new, c.B);
+hipError_t launch_append_decode(const CacheView& c, const AppendInputs& in, hipStream_t st) {
+  hipLaunchKernelGGL(append_decode_kernel, dim3(c.B), dim3(256), 0, st, c, in);
+  return hipGetLastError();
+}
+
+hipError_t launch_update_lengths(const CacheView& c, const AppendInputs& in, hipStream_t st) {
+  hipLaunchKernelGGL(update_lengths_kernel, dim3((c.B + 255) / 256), dim3(256), 0, st, c, in);
   return hipGetLastError();
 }
 

@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, c16 = lane & 15, grp = lane >> 4;
-  const int L = c.seq_len[b];
+  const int L = min(max(c.seq_len[b], 0), c.T);  // clamped: never past the capacity
   const int nsplit_b = (L + p.tokens_per_split - 1) / p.tokens_per_split;
   if (split > 0 && split >= nsplit_b) return;  // beyond this sequence (split 0 always runs)
   const int Q = KAXIS ? L - L % c.R : L;
@@ -734,7 +734,7 @@ __global__ __launch_bounds__(128) void combine_kernel(CacheView c, AttnPlan p, c
                                                       float* __restrict__ out) {
   const int bq = blockIdx.x, ch = threadIdx.x;
   const int b = bq / p.Hq;
-  const int L = c.seq_len[b];
+  const int L = min(max(c.seq_len[b], 0), c.T);  // clamped: never past the capacity
   const int ns = (L + p.tokens_per_split - 1) / p.tokens_per_split;
   if (ns <= 1) return;  // written directly by the attention kernel
   const float* part = ws + (size_t)bq * p.n_split * kPartialFloats;

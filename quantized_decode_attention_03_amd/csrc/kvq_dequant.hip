@@ -18,7 +18,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(CacheView c, uint16_t* kou
   const int tid = threadIdx.x;
   const int tau = tid >> 3, c0 = (tid & 7) * 16;
   const int t = j * kBlock + tau;
-  const int L = c.seq_len[b];
+  const int L = min(max(c.seq_len[b], 0), c.T);  // clamped: never past the capacity
   const int Q = c.kaxis == 0 ? L : L - L % c.R;
   const size_t bh = (size_t)b * c.H + h;
   const size_t o = (((size_t)b * c.T + t) * c.H + h) * kD;

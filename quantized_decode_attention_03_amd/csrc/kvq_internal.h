@@ -28,9 +28,10 @@ struct CacheView {
 };
 
 struct AppendInputs {
-  const uint16_t* k_new;       // fp16 [N][H][D]
+  const uint16_t* k_new;       // fp16 [rows][H][D]
   const uint16_t* v_new;
   const int32_t* cu_new;       // [B+1]
+  int rows;                    // rows of k_new / v_new (sum of the new counts)
 };
 
 // Launchers; each returns the hipError_t of its launch.
@@ -38,8 +39,11 @@ hipError_t launch_flush_keys(const CacheView& c, const AppendInputs& in,
                              int max_blocks, hipStream_t st);
 hipError_t launch_append_tokens(const CacheView& c, const AppendInputs& in,
                                 int max_blocks, hipStream_t st);
-hipError_t launch_update_lengths(const CacheView& c, const int32_t* cu_new,
+hipError_t launch_update_lengths(const CacheView& c, const AppendInputs& in,
                                  hipStream_t st);
+// One new token per sequence: append and length update in one launch.
+hipError_t launch_append_decode(const CacheView& c, const AppendInputs& in,
+                                hipStream_t st);
 hipError_t launch_dequantize(const CacheView& c, uint16_t* k_out,
                              uint16_t* v_out, hipStream_t st);
 

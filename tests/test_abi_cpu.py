@@ -135,3 +135,76 @@ def test_status_strings():
     for s in range(6):
         assert N.status_string(s)
     assert N.status_string(N.KVQ_ECAPACITY) == "append exceeds cache capacity"
+
+
+def test_sizes_take_64_bit_token_counts():
+    # the sizing calls take int64_t max_tokens: values past int32 reach the
+    # library intact and are refused as unsupported, not truncated
+    c = _cfg()
+    L = N.lib()
+    out = N.kvq_sizes()
+    for big in (1 << 31, (1 << 32) + 32, 1 << 40):
+        assert L.kvq_cache_sizes(ctypes.byref(c.c()), 1, big, ctypes.byref(out)) == N.KVQ_EUNSUPPORTED
+        assert kvq_workspace_bytes(c, 1, big) == 0
+    # the largest capacity a cache can describe is still accepted
+    assert kvq_cache_sizes(c, 1, 1 << 24)["k_codes"] == 8 * (1 << 24) * 64
+    assert kvq_workspace_bytes(c, 1, 1 << 24) > 0
+    assert L.kvq_cache_sizes(ctypes.byref(c.c()), 1, (1 << 24) + 32, ctypes.byref(out)) == N.KVQ_EUNSUPPORTED
+
+
+def test_binding_rejects_bad_tensors():
+    """The binding checks dtype, device, contiguity and exact shape of every
+    tensor before any pointer crosses the ABI (CPU tensors are refused as not
+    on the device, so nothing here launches)."""
+    import torch
+    import quantized_decode_attention_03_amd as K
+
+    class _Cache:  # the attributes the binding reads
+        batch, max_tokens = 2, 64
+        cfg = _cfg()
+        device = torch.device("cuda", 0)
+
+    cache = _Cache()
+    k = torch.zeros((3, 8, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="device tensor"):
+        K.kvq_append(cache, k, k, None, [2, 1])
+    with pytest.raises(ValueError, match="counts for a batch"):
+        K.kvq_append(cache, k, k, None, [3])
+    with pytest.raises(ValueError, match="negative"):
+        K.kvq_append(cache, k, k, None, [4, -1])
+    q = torch.zeros((2, 32, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="device tensor"):
+        K.kvq_decode_attention(cache, q, q.float(), 0.1, torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="device tensor"):
+        K.kvq_dequantize(cache, q, q)
+    # the checks themselves, on tensors that pass the device test
+    chk = K._check
+    with pytest.raises(ValueError, match="torch tensor"):
+        chk(3, "x", torch.float16)
+
+
+def test_binding_check_rules(monkeypatch):
+    """Dtype, contiguity, shape and device rules of the binding's tensor check,
+    exercised with CPU tensors that pretend to be on the device."""
+    import torch
+    import quantized_decode_attention_03_amd as K
+
+    class _Dev(torch.Tensor):
+        pass
+
+    def dev(t):
+        d = t.as_subclass(_Dev)
+        return d
+
+    monkeypatch.setattr(_Dev, "is_cuda", property(lambda self: True))
+    monkeypatch.setattr(_Dev, "device", property(lambda self: torch.device("cuda", 0)))
+    t = dev(torch.zeros((4, 8, 128), dtype=torch.float16))
+    K._check(t, "t", torch.float16, (4, 8, 128), torch.device("cuda", 0))
+    with pytest.raises(ValueError, match="dtype"):
+        K._check(t, "t", torch.float32, (4, 8, 128))
+    with pytest.raises(ValueError, match="shape"):
+        K._check(t, "t", torch.float16, (5, 8, 128))
+    with pytest.raises(ValueError, match="contiguous"):
+        K._check(dev(torch.zeros((8, 4, 128), dtype=torch.float16)).transpose(0, 1), "t", torch.float16)
+    with pytest.raises(ValueError, match="the cache is on"):
+        K._check(t, "t", torch.float16, None, torch.device("cuda", 1))
