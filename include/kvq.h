@@ -105,10 +105,11 @@
  *
  * Environment (read by the library; both optional)
  *   KVQ_DEBUG=1         synchronize after every launch and print HIP errors.
- *   KVQ_SPLIT_TOKENS=n  force the split length of kvq_decode_attention to n
- *                       tokens (rounded up to a multiple of 32, at least 256)
- *                       instead of the built-in plan; for checks that vary the
- *                       split count on one input.
+ *   KVQ_SPLIT_TOKENS=n  make every workgroup of kvq_decode_attention take n
+ *                       tokens' worth of 32-token tiles (at least 8 tiles)
+ *                       instead of the built-in plan (as many workgroups as
+ *                       the device holds at once); for checks that vary the
+ *                       split of the work on one input.
  *
  * Errors
  *   Arguments are validated on the host before anything is launched; an error
@@ -183,9 +184,10 @@ typedef struct kvq_sizes {
 kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch,
                            int64_t max_tokens, kvq_sizes* out_host);
 
-/* Bytes of device workspace kvq_decode_attention needs for this shape
- * (split-K partial results). 0 on a bad configuration or size (the rules of
- * kvq_cache_sizes). Pure host function. */
+/* Bytes of device workspace kvq_decode_attention needs for this shape:
+ * partial results (m, l, o[128] in fp32) of the work ranges that share a
+ * (sequence, query head), at most max_tokens/256 + 2 of them. 0 on a bad
+ * configuration or size (the rules of kvq_cache_sizes). Pure host function. */
 size_t kvq_workspace_bytes(const kvq_config* cfg, int32_t batch,
                            int64_t max_tokens);
 
@@ -209,11 +211,15 @@ kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache,
  *               * V_hat[b][kv][t],   kv = h / (Hq / H), t < seq_len[b],
  * where K_hat / V_hat are the dequantized codes (plus sparse entries), and
  * residual keys are the stored fp16 values. A sequence with no tokens gets
- * out = 0. ws is device workspace of at least kvq_workspace_bytes(cfg,
- * cache->batch, cache->max_tokens) bytes for split partial results; its
- * contents need no initial value. Calls that share a workspace must be
- * ordered on one stream.
- * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EWORKSPACE, KVQ_EHIP. */
+ * out = 0. The work (every 32-token tile of every (sequence, KV head)) is
+ * cut into equal contiguous ranges, one per workgroup; pairs whose tiles span
+ * several ranges are merged by a log-sum-exp in a second kernel. ws is device
+ * workspace of at least kvq_workspace_bytes(cfg, cache->batch,
+ * cache->max_tokens) bytes for those partial results; its contents need no
+ * initial value. Calls that share a workspace must be ordered on one stream.
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED (also when batch * n_kv_heads *
+ * max_tokens / 32 exceeds 2^31 - 1, the device's tile index range),
+ * KVQ_EWORKSPACE, KVQ_EHIP. */
 kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 const void* q, float* out, float softmax_scale,
                                 void* ws, size_t ws_bytes,

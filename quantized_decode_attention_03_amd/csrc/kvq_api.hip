@@ -57,55 +57,59 @@ int compute_units() {
   return n;
 }
 
-// Split plan: 32-token tiles per split. Each (sequence, KV head) is cut into
-// splits of `tps` tiles, one workgroup each; `slots` workgroups run at once.
-// The makespan is estimated as whole rounds of slots, each as long as one
-// full split plus a fixed per-workgroup overhead (first-tile latency, merge),
-// and the split length with the smallest estimate wins (ties: the longer).
-// Splits are at least kMinSplitTiles long, which bounds their number by the
-// workspace size.
-int plan_tiles_per_split(const kvq_cache* cache, int n_kv_heads, int64_t slots) {
-  constexpr int kOverheadTiles = 4;
-  int max_tiles = 0;
-  for (int b = 0; b < cache->batch; ++b)
-    max_tiles = std::max(max_tiles, (int)((cache->len_host[b] + kBlock - 1) / kBlock));
-  if (max_tiles <= kMinSplitTiles) return std::max(max_tiles, 1);
-  int best_tps = max_tiles, prev = -1;
-  double best = 1e300;
-  for (int ns = 1;; ++ns) {
-    const int tps = (max_tiles + ns - 1) / ns;
-    if (tps < kMinSplitTiles) break;
-    if (tps == prev) continue;
-    prev = tps;
-    int64_t wgs = 0, work = 0;
-    for (int b = 0; b < cache->batch; ++b) {
-      const int t = (int)((cache->len_host[b] + kBlock - 1) / kBlock);
-      wgs += std::max(1, (t + tps - 1) / tps);
-      work += t;
-    }
-    wgs *= n_kv_heads;
-    work *= n_kv_heads;
-    const double wg_time = tps + kOverheadTiles;
-    const double rounds = std::ceil((double)(work + wgs * kOverheadTiles) / ((double)slots * wg_time));
-    const double cost = std::max(rounds, 1.0) * wg_time;
-    if (cost < best) {
-      best = cost;
-      best_tps = tps;
+// Attention work plan from the host's lengths (the appends keep them equal
+// to the device's): U = 32-token tiles of quantized keys of all (sequence,
+// KV head) pairs, and the workgroup count, as many as the chip holds at once,
+// each taking U / n contiguous tiles, but never fewer than kMinUnitsPerWg
+// (which bounds the partial results per pair by the workspace size).
+// KVQ_SPLIT_TOKENS=n (read on every call) sets the tiles per workgroup to
+// n/32 instead, for checks that vary the work split on one input. The merge
+// kernel runs when a pair spans several workgroups or a sequence is empty
+// (its output is written as 0 there).
+int64_t wg_of_unit_host(int64_t u, int64_t U, int64_t nwg) { return ((u + 1) * nwg + U - 1) / U - 1; }
+
+void plan_attention(const kvq_config* cfg, const kvq_cache* cache, int64_t slots, AttnPlan* p) {
+  const int64_t H = cfg->n_kv_heads;
+  const bool chan = cfg->k_axis == KVQ_AXIS_CHANNEL;
+  // units of one (sequence, KV head): its quantized 32-token tiles, or one
+  // unit for residual keys alone
+  auto units = [&](int b) -> int64_t {
+    const int64_t L = cache->len_host[b];
+    const int64_t Q = chan ? L - L % cfg->k_residual_tokens : L;
+    return Q > 0 ? (Q + kBlock - 1) / kBlock : (L > 0 ? 1 : 0);
+  };
+  int64_t U = 0;
+  bool need = false;
+  for (int b = 0; b < cache->batch; ++b) {
+    U += H * units(b);
+    need = need || cache->len_host[b] == 0;
+  }
+  int64_t per = kMinUnitsPerWg;
+  if (const char* e = getenv("KVQ_SPLIT_TOKENS")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v > 0) per = std::max<int64_t>((v + kBlock - 1) / kBlock, kMinUnitsPerWg);
+  }
+  int64_t nwg = 0;
+  if (U > 0) nwg = per > kMinUnitsPerWg ? std::max<int64_t>(1, U / per)
+                                         : std::min<int64_t>(std::max<int64_t>(1, slots), std::max<int64_t>(1, U / per));
+  p->units = U;
+  p->n_wg = (int)nwg;
+  p->max_parts = max_parts_for(cache->max_tokens);
+  if (nwg > 1) {
+    int64_t base = 0;
+    for (int b = 0; b < cache->batch && !need; ++b) {
+      const int64_t nt = units(b);
+      for (int64_t h = 0; h < H && nt > 0; ++h) {
+        const int64_t s0 = base + h * nt;
+        if (wg_of_unit_host(s0, U, nwg) != wg_of_unit_host(s0 + nt - 1, U, nwg)) {
+          need = true;
+          break;
+        }
+      }
+      base += H * nt;
     }
   }
-  return best_tps;
-}
-
-// Split length forced through the environment (KVQ_SPLIT_TOKENS, read on
-// every call), for checks that vary the split count on one input; 0 when
-// unset. Never below kMinSplitTokens, so the workspace bound still holds.
-int split_override_tiles() {
-  const char* e = getenv("KVQ_SPLIT_TOKENS");
-  if (!e || !*e) return 0;
-  const long v = strtol(e, nullptr, 10);
-  if (v <= 0) return 0;
-  const long tiles = std::max<long>((v + kBlock - 1) / kBlock, kMinSplitTiles);
-  return (int)std::min<long>(tiles, 1L << 20);
+  p->need_combine = need ? 1 : 0;
 }
 
 kvq_status check_config(const kvq_config* cfg) {
@@ -216,7 +220,7 @@ kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch, int64_t max_tok
 
 size_t kvq_workspace_bytes(const kvq_config* cfg, int32_t batch, int64_t max_tokens) {
   if (check_config(cfg) != KVQ_OK || check_shape(batch, max_tokens) != KVQ_OK) return 0;
-  return (size_t)batch * cfg->n_q_heads * max_splits_for((int)max_tokens) * kPartialFloats * sizeof(float);
+  return (size_t)batch * cfg->n_q_heads * max_parts_for((int)max_tokens) * kPartialFloats * sizeof(float);
 }
 
 kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new, const void* v_new,
@@ -272,17 +276,13 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   if (!q || !out || !ws || !aligned(q) || !aligned(out) || !aligned(ws)) return KVQ_EINVAL;
   if (ws_bytes < kvq_workspace_bytes(cfg, cache->batch, cache->max_tokens)) return KVQ_EWORKSPACE;
   const CacheView v = view_of(cfg, cache);
+  // tile indices are 32-bit on the device
+  if ((int64_t)cache->batch * cfg->n_kv_heads * (cache->max_tokens / kBlock) > INT32_MAX) return KVQ_EUNSUPPORTED;
   AttnPlan p;
   p.Hq = cfg->n_q_heads;
   p.group = cfg->n_q_heads / cfg->n_kv_heads;
   p.scale = softmax_scale;
-  int tps = plan_tiles_per_split(cache, cfg->n_kv_heads,
-                                 compute_units() * attention_blocks_per_cu(v, p.group));
-  if (const int forced = split_override_tiles()) tps = forced;
-  int lmax = 0;
-  for (int b = 0; b < cache->batch; ++b) lmax = std::max(lmax, (int)cache->len_host[b]);
-  p.tokens_per_split = tps * kBlock;
-  p.n_split = std::max(1, (lmax + p.tokens_per_split - 1) / p.tokens_per_split);
+  plan_attention(cfg, cache, (int64_t)compute_units() * attention_blocks_per_cu(v, p.group), &p);
   hipStream_t st = (hipStream_t)stream;
   return after_launch(launch_decode_attention(v, p, (const uint16_t*)q, out, (float*)ws, st), st);
 }

@@ -14,36 +14,51 @@
 //   S^T[token, col] = sum_c A[token, c] * B[c, col]
 //   O[row, c]       = sum_t P[row, t] * V[t, c]
 // Codes enter the matrix cores as their own bit patterns: a stored code u
-// placed at bit SH of an fp16 (u << SH < 2^10) is the subnormal u * 2^(SH-24),
-// which the matrix cores multiply exactly. Unpacking is therefore only shifts
-// and masks. SH is 8 for 2-bit codes, 4 for 4-bit and 0 for 8-bit: chains of
-// accumulating MFMAs lose accuracy when the operands are very small (measured:
-// 2-bit codes at u * 2^-24 gave key-score errors near 2e-3, at u * 2^-16 near
-// 5e-6 on the same data), so small codes sit as high in the subnormal range
-// as the shift-and-mask extraction allows. The zero points are not subtracted element by element; their
-// contribution is a rank-one term that runs on the matrix cores as well:
+// masked at bit sh of an fp16 half (sh + bits <= 10) is the subnormal
+// u * 2^(sh-24), which the matrix cores multiply exactly. Chains of
+// accumulating MFMAs have an absolute error floor, so the products must not be
+// small (measured: 2-bit codes at u * 2^-24 gave key-score errors near 2e-3,
+// at u * 2^-16 near 5e-6); every product is kept at the magnitude it has with
+// all codes at bit SH, the variant's code unit 2^(SH-24): SH is 8 for 2-bit,
+// 4 for 4-bit and 0 for 8-bit codes.
+//   Values: every pair of codes is moved to bit SH (a shift and a mask).
+//   Channel-axis keys: each pair stays where a single mask reaches it (plus
+//     one shift per word for the fields above bit 10), and the factor
+//     2^(SH - sh) is folded into the scaled query of its channel, which has
+//     the fp16 range to spare (the softmax weights, the value product's other
+//     operand, do not).
+//   Token-axis keys: their query operand is the raw fp16 query, which cannot
+//     absorb a factor without rounding, so they take the value treatment.
+//
+// Zero points are not subtracted element by element:
 //   keys, channel axis: x = s_c (u - z'_c); B = q * s_c (scaled query, split
-//     into fp16 hi and lo parts in columns h and g + h, ~22 bits); the term
-//     sum_c z'_c B[c, col] is the same for every token of a block and seeds
-//     the accumulator (an A operand whose rows all hold -z', in the same
-//     code-step units as the codes);
+//     into fp16 hi and lo parts); the term sum_c z'_c B[c, col] is the same
+//     for every token of a block and seeds the accumulator (an A operand whose
+//     rows all hold -z');
 //   keys, token axis: x = s_t (u - z'_t); B = raw fp16 query (exact); the
-//     term z'_t sum_c q_c seeds the accumulator the same way (row t of the A
-//     operand holds -z'_t); s_t multiplies the scores afterwards;
+//     term z'_t * sum_c q_c is one FMA per score; s_t multiplies the score;
 //   values, token axis: x = s_t (u - z'_t); P = p_t * s_t * 2^kv as hi/lo rows
 //     h and g + h; the product with a B operand whose columns all hold z'_t
 //     is subtracted once at the end.
+// The hi and lo parts of the scaled query sit in different columns of one B
+// operand (column n: head n mod g, hi part when n / g is even), so one MFMA
+// covers both; one DPP add across lanes n and n - g of a 16-lane row sums
+// them, and every lane then holds the full score of its column's head.
 // The factor 2^kv keeps p * s inside fp16: it is one exponent per wavefront,
 // raised lazily (rarely) when a larger value scale shows up, like the softmax
 // reference.
 //
-// Work split: grid (split, KV head, sequence), 4 wavefronts per workgroup,
-// each wavefront owns every 4th 32-token tile of the split and keeps its own
-// online softmax; the wavefronts merge through LDS. Sequences longer than one
-// split leave (m, l, o) partials in the workspace that a second, small kernel
-// merges with a log-sum-exp. (Merging in the last-arriving workgroup instead
-// needs device-scope fences, whose L2 writeback and invalidation cost far more
-// than the extra launch on this chip.)
+// Work split: a fixed grid of workgroups (as many as the chip holds at once),
+// each taking an equal, contiguous range of the 32-token tiles of all
+// (sequence, KV head) pairs, so ragged lengths leave no workgroup idle and
+// each pays its start-up latency once. Within a range, a workgroup walks the
+// (sequence, KV head) segments it covers; its 4 wavefronts take every 4th tile
+// of a segment, keep their own online softmax and merge through LDS. A segment
+// that is a whole (sequence, KV head) writes the output; the others leave
+// (m, l, o) partials in the workspace that a second, small kernel merges with
+// a log-sum-exp. (Merging in the last-arriving workgroup instead needs
+// device-scope fences, whose L2 writeback and invalidation cost far more than
+// the extra launch on this chip.)
 #include <algorithm>
 #include <atomic>
 
@@ -58,11 +73,15 @@ typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kTwoM24 = 1.f / 16777216.f;     // 2^-24, the smallest fp16 subnormal
+// LDS bytes per wavefront for tile slots plus the wavefront's operand area:
+// 2 or 3 slots of the 4- and 2-bit tiles (a tile in flight while another is
+// computed), about 47 KiB per 4-wavefront workgroup. Measured on the three
+// KIVI workloads against budgets of 16 and 20 KiB (more slots, fewer
+// workgroups per compute unit): this one was as fast or faster on each.
 #ifndef KVQ_WAVE_LDS_BUDGET
-#define KVQ_WAVE_LDS_BUDGET 19968
+#define KVQ_WAVE_LDS_BUDGET 12000
 #endif
-constexpr int kWaveBudget = KVQ_WAVE_LDS_BUDGET;  // LDS bytes per wavefront
+constexpr int kWaveBudget = KVQ_WAVE_LDS_BUDGET;
 
 struct Frag {  // 8 fp16 MFMA operand values as 4 packed pairs
   uint32_t p[4];
@@ -78,9 +97,8 @@ __device__ __forceinline__ float f16hi(uint32_t w) { return (float)as_h2(w)[1]; 
 __device__ __forceinline__ float mul_lo(float x, uint32_t w) { return __builtin_fmaf(x, f16lo(w), 0.f); }
 
 // fp16 pair (a * m + c, b * m + c) of the fp16 halves of w (one v_pk_fma_f16)
-__device__ __forceinline__ uint32_t pk_fma16(uint32_t w, _Float16 m, _Float16 c) {
-  const h2v mm = {m, m}, cc = {c, c};
-  return as_u32(__builtin_elementwise_fma(as_h2(w), mm, cc));
+__device__ __forceinline__ uint32_t pk_fma16(uint32_t w, h2v m, h2v c) {
+  return as_u32(__builtin_elementwise_fma(as_h2(w), m, c));
 }
 
 __device__ __forceinline__ f4v mfma(const Frag& a, const Frag& b, f4v c) {
@@ -102,52 +120,136 @@ __device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
 
-// Bit position of a code inside its fp16 operand (the code's value is
-// u * 2^(SH-24)).
+// 2^e as an exact float (compile-time)
+__host__ __device__ constexpr float pow2f(int e) {
+  float r = 1.f;
+  for (int i = 0; i < e; ++i) r *= 2.f;
+  for (int i = 0; i < -e; ++i) r *= 0.5f;
+  return r;
+}
+__device__ __forceinline__ h2v h2_splat(uint16_t bits) {
+  const _Float16 x = __builtin_bit_cast(_Float16, bits);
+  return h2v{x, x};
+}
+
+// ---- code operands -----------------------------------------------------------
+
+// Code unit of the key and value operands: 2^(SH-24).
+template <int BITS> constexpr int unit_shift() { return BITS == 2 ? 8 : (BITS == 4 ? 4 : 0); }
+
+// Channel of k-slot pair p (first or second slot) in chunk j of lane group
+// grp, for key codes of BITS bits. Key rows are channel-packed with the low
+// bits first.
 template <int BITS>
-constexpr int code_shift() { return BITS == 2 ? 8 : (BITS == 4 ? 4 : 0); }
+__device__ __forceinline__ int key_channel(int grp, int j, int p, int second) {
+  if constexpr (BITS == 8) return 32 * grp + 8 * j + 2 * p + second;
+  if constexpr (BITS == 4) return 32 * grp + 8 * j + p + 4 * second;
+  return 32 * grp + 16 * (j >> 1) + 4 * (j & 1) + p + 8 * second;
+}
+
+// Bit position sh of the codes of key k-slot pair p in chunk j. U (uniform):
+// every pair at the unit shift.
+template <int KB, bool U>
+__host__ __device__ constexpr int key_sh(int j, int p) {
+  if (KB == 8) return 0;
+  if (U) return unit_shift<KB>();
+  if (KB == 4) return (p & 1) ? 4 : 0;
+  return ((j & 1) && p == 0) ? 8 : 2 * p + 2;
+}
 
 // Two fields of BITS bits, at bit n and n + 16 of w, moved to bit SH of each
-// half: the fp16 pair (u0 * 2^(SH-24), u1 * 2^(SH-24)).
+// half.
 template <int BITS>
 __device__ __forceinline__ uint32_t field_pair(uint32_t w, int n) {
-  constexpr int SH = code_shift<BITS>();
+  constexpr int SH = unit_shift<BITS>();
   constexpr uint32_t kMask = (((1u << BITS) - 1u) << SH) * 0x10001u;
   if (n == SH) return w & kMask;
   if (n < SH) return (w << (SH - n)) & kMask;
   return (w >> (n - SH)) & kMask;
 }
 
-// 8 codes -> 4 fp16 code pairs, k-slot pairs (2p, 2p+1) taking:
-//   BITS 4: word a, nibbles (p, p+4);
-//   BITS 2: word a, 2-bit fields (4y + p, 4y + p + 8), y = 0 or 1;
-//   BITS 8: bytes (2p, 2p+1) of the 8 bytes a, b.
-template <int BITS>
-__device__ __forceinline__ Frag codes8(uint32_t a, uint32_t b, int y) {
+// Key operand of chunk j from the lane's code words of one token row (the
+// lane group's 32 channels): KB words for 4/2-bit codes, 2 per chunk for 8-bit.
+//   4-bit: word j, nibbles (p, p+4) -> pair p; per-pair positions: nibbles
+//          0/1 and 4/5 masked in place (sh 0, 4), nibbles 2/3 and 6/7 after
+//          one shift by 8.
+//   2-bit: word j/2; fields (n, n+16), n = 8 (j odd) + 2p; per-pair
+//          positions: j even, all four after one shift left by 2 (sh 2p + 2);
+//          j odd, field 8 in place (sh 8), fields 10..14 after one shift
+//          right by 6 (sh 2p + 2).
+//   8-bit: bytes (2p, 2p+1) of the chunk's two words (sh 0).
+template <int KB, bool U>
+__device__ __forceinline__ Frag key_frag(const uint32_t* kc, int j) {
   Frag f;
-  if constexpr (BITS == 4) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) f.p[p] = field_pair<4>(a, 4 * p);
-  } else if constexpr (BITS == 2) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) f.p[p] = field_pair<2>(a, 8 * y + 2 * p);
-  } else {
+  if constexpr (KB == 8) {
+    const uint32_t a = kc[2 * j], b = kc[2 * j + 1];
     f.p[0] = perm(0u, a, 0x0C010C00u);
     f.p[1] = perm(0u, a, 0x0C030C02u);
     f.p[2] = perm(0u, b, 0x0C010C00u);
     f.p[3] = perm(0u, b, 0x0C030C02u);
+  } else if constexpr (U) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      f.p[p] = KB == 4 ? field_pair<4>(kc[j], 4 * p) : field_pair<2>(kc[j >> 1], 8 * (j & 1) + 2 * p);
+  } else if constexpr (KB == 4) {
+    const uint32_t w = kc[j], t = w >> 8;
+    f.p[0] = w & 0x000F000Fu;
+    f.p[1] = w & 0x00F000F0u;
+    f.p[2] = t & 0x000F000Fu;
+    f.p[3] = t & 0x00F000F0u;
+  } else {
+    const uint32_t w = kc[j >> 1];
+    if ((j & 1) == 0) {
+      const uint32_t t = w << 2;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) f.p[p] = t & (0x00030003u << (2 * p + 2));
+    } else {
+      const uint32_t t = w >> 6;
+      f.p[0] = w & 0x03000300u;
+#pragma unroll
+      for (int p = 1; p < 4; ++p) f.p[p] = t & (0x00030003u << (2 * p + 2));
+    }
   }
   return f;
 }
 
-// Channel of k-slot pair p (first or second slot) in chunk j of lane group
-// grp, for key codes of BITS bits. Key rows are channel-packed with the low
-// bits first; this is the order codes8() produces.
-template <int BITS>
-__device__ __forceinline__ int key_channel(int grp, int j, int p, int second) {
-  if constexpr (BITS == 8) return 32 * grp + 8 * j + 2 * p + second;
-  if constexpr (BITS == 4) return 32 * grp + 8 * j + p + 4 * second;
-  return 32 * grp + 16 * (j >> 1) + 4 * (j & 1) + p + 8 * second;
+// Value operand: 8 tokens of one channel, every code at bit SH. k-slot pair
+// p holds tokens (p, p+4) for 4/2-bit values, (2p, 2p+1) for 8-bit ones.
+//   4-bit: the record word (nibble i = token i), nibbles (p, p+4);
+//   2-bit: the 16-bit record spread to bytes 1 and 3 (tokens 0..3, 4..7),
+//          fields (8 + 2p, 24 + 2p);
+//   8-bit: bytes of two words.
+template <int VB>
+__device__ __forceinline__ Frag val_frag(uint32_t a, uint32_t b) {
+  Frag f;
+  if constexpr (VB == 8) {
+    f.p[0] = perm(0u, a, 0x0C010C00u);
+    f.p[1] = perm(0u, a, 0x0C030C02u);
+    f.p[2] = perm(0u, b, 0x0C010C00u);
+    f.p[3] = perm(0u, b, 0x0C030C02u);
+  } else if constexpr (VB == 4) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) f.p[p] = field_pair<4>(a, 4 * p);
+  } else {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) f.p[p] = field_pair<2>(a, 8 + 2 * p);
+  }
+  return f;
+}
+// The lane's value record words of one channel, as val_frag takes them.
+template <int VB>
+__device__ __forceinline__ void val_words(const uint8_t* rec, int grp, uint32_t& lo, uint32_t& hi) {
+  if constexpr (VB == 4) {
+    lo = reinterpret_cast<const uint32_t*>(rec)[grp];
+    hi = 0u;
+  } else if constexpr (VB == 8) {
+    const uint2 x = reinterpret_cast<const uint2*>(rec)[grp];
+    lo = x.x;
+    hi = x.y;
+  } else {
+    lo = perm(0u, reinterpret_cast<const uint16_t*>(rec)[grp], 0x010C000Cu);
+    hi = 0u;
+  }
 }
 
 // Geometry of one 32-token tile as staged in LDS:
@@ -169,14 +271,17 @@ struct Geom {
   static constexpr int kBytes = kK + kV + kVm + kKm + kSp;
   static constexpr int kLoads = kK / 1024 + kV / 1024 + (SPARSE ? 3 : 2);  // DMA instructions per tile
   // the key-product B operand and zero-point operand (channel axis only)
-  static constexpr int kWaveLds = KAXIS ? (4 * (2 * G + 1) * 4 * 16 + 4 * 4 * 4 * 4) : 0;
-  // tile slots per wavefront: as many as fit the per-wavefront LDS budget
-  // (kWaveBudget, chosen so that several 4-wavefront workgroups share a CU's
-  // 160 KiB), between 2 and 4
-  static constexpr int kSlotsFit = (kWaveBudget - kWaveLds) / kBytes;
-  static constexpr int kSlots = kSlotsFit < 2 ? 2 : (kSlotsFit > 4 ? 4 : kSlotsFit);
+  static constexpr int kWaveLds = KAXIS ? (4 * (2 * G) * 4 * 16 + 4 * 4 * 4 * 4) : 0;
+  // tile slots per wavefront: as many as fit the per-wavefront budget, 2 to 6
+  static constexpr int kSlotsFit = (kWaveBudget - kWaveLds - (SPARSE ? G * kD : 0)) / kBytes;
+  static constexpr int kSlots = kSlotsFit < 2 ? 2 : (kSlotsFit > 6 ? 6 : kSlotsFit);
+  static constexpr int kQLoads = G == 8 ? 2 : 1;      // DMA instructions for the query heads
   static_assert(kK % 1024 == 0 && kV % 1024 == 0, "1 KiB load granularity");
   static_assert(kMetaLanes <= 64, "metadata fits one load");
+  static_assert((kSlots - 1) * kLoads <= 63, "waits fit the vmcnt field");
+  // a residual tile (16 fp16 key rows, the value block and scales) fits the slots
+  static_assert(!KAXIS || 4096 + kV + 128 <= kSlots * kBytes, "residual tile fits the slots");
+  static_assert(kBytes >= G * kD * 2, "the query heads fit one tile slot");
 };
 
 // Buffer resource (V#) over `bytes` bytes at `base`: a raw descriptor (stride
@@ -210,14 +315,27 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
+// Wait until at most n * K loads (n <= 5) are outstanding.
+template <int K>
+__device__ __forceinline__ void wait_vm_n(int n) {
+  switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<K>(); break;
+    case 2: wait_vm<2 * K>(); break;
+    case 3: wait_vm<3 * K>(); break;
+    case 4: wait_vm<4 * K>(); break;
+    default: wait_vm<5 * K>(); break;
+  }
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
 // LDS per wavefront for channel-axis keys: the B operand of the key product
-// for the current block (hi rows 0..G-1, lo rows G..2G-1, an all-zero row 2G;
-// [grp][row][chunk] fragments) and the zero-point A operand, -z' in code-step units per
-// channel ([grp][chunk][pair]).
+// for the current block (hi rows 0..G-1, lo rows G..2G-1; [grp][row][chunk]
+// fragments) and the zero-point A operand, -z' per channel in the unit of its
+// codes ([grp][chunk][pair]).
 template <int G>
 struct WaveLds {
-  Frag qb[4][2 * G + 1][4];
+  Frag qb[4][2 * G][4];
   uint32_t zc[4][4][4];
 };
 
@@ -239,15 +357,18 @@ __device__ __forceinline__ float grp_sum(float v) {
   return v + __shfl_xor(v, 32, 64);
 }
 
+// x plus x of lane n - G (mod 16) of the same 16-lane row (DPP row_ror:G):
+// lanes n and n -+ G hold the hi and lo parts of the same head's score.
+template <int G>
+__device__ __forceinline__ float add_ror(float x) {
+  const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + G, 0xF, 0xF, false);
+  return x + __builtin_bit_cast(float, y);
+}
+
 // The softmax reference m of a head moves only when a score exceeds it by
 // more than 2^kLazy (log2 units), so most tiles need no cross-lane maximum and
 // no rescaling; weights stay <= 2^kLazy.
 constexpr float kLazy = 8.f;
-
-// The value-scale factor 2^kv, kv = kKvTop - E, is set from the largest fp16
-// biased exponent E among the value scales seen so far, so that s * 2^kv < 2^6
-// and the P operand p * s * 2^kv < 2^14 stays inside fp16.
-constexpr int kKvTop = 20;
 
 // Token (0..31 within the tile) of A row m in MFMA row block e: row block e
 // holds tokens 8*(m/4) + 4e + m%4, so the output lane group g ends up with
@@ -255,6 +376,90 @@ constexpr int kKvTop = 20;
 __device__ __forceinline__ int a_token(int e, int m) { return 8 * (m >> 2) + 4 * e + (m & 3); }
 
 __device__ __forceinline__ uint16_t umax16(uint16_t a, uint16_t b) { return a > b ? a : b; }
+
+// Units of work: the 32-token tiles of quantized keys of every (sequence, KV
+// head), ordered by sequence, then KV head, then tile; sequence b contributes
+// H * ceil(Q_b / 32) units (Q_b = tokens whose keys are codes: all of them on
+// the token axis, L_b - L_b mod R on the channel axis), or H units when it
+// holds residual keys only. The residual fp16 keys of a (sequence, KV head)
+// go with its last unit. Workgroup i of n takes the contiguous units
+// [i U / n, (i+1) U / n), so every workgroup gets the same amount of work
+// whatever the lengths, and walks the (sequence, KV head) segments its range
+// covers.
+__device__ __forceinline__ int seq_len_of(const CacheView& c, int b) {
+  return min(max(c.seq_len[b], 0), c.T);  // clamped: never past the capacity
+}
+__device__ __forceinline__ int quant_len(const CacheView& c, int L) { return c.kaxis ? L - L % c.R : L; }
+__device__ __forceinline__ int units_of(const CacheView& c, int L) {
+  const int Q = quant_len(c, L);
+  return Q > 0 ? (Q + kBlock - 1) / kBlock : (L > 0 ? 1 : 0);
+}
+__device__ __forceinline__ int seq_tiles(const CacheView& c, int b) { return units_of(c, seq_len_of(c, b)); }
+
+// Workgroup whose range holds unit u.
+__device__ __forceinline__ int wg_of_unit(int u, int64_t U, int nwg) {
+  return (int)(((int64_t)(u + 1) * nwg + U - 1) / U) - 1;
+}
+
+struct UnitPos {
+  int b;     // sequence holding the unit (B if the unit is past the last one)
+  int base;  // its first unit
+};
+
+// The sequence holding unit u: a wavefront-wide scan of the sequences' unit
+// counts, 256 sequences (4 per lane) at a time. Every lane returns the same.
+__device__ UnitPos locate_unit(const CacheView& c, int u) {
+  const int lane = threadIdx.x & 63;
+  int acc = 0;
+  for (int cb = 0; cb < c.B; cb += 256) {
+    int n[4], sum = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int bb = cb + 4 * lane + r;
+      n[r] = bb < c.B ? c.H * seq_tiles(c, bb) : 0;
+      sum += n[r];
+    }
+    int incl = sum;  // inclusive scan over the lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const int chunk = __shfl(incl, 63, 64);
+    if (u < acc + chunk) {
+      const uint64_t over = __builtin_amdgcn_ballot_w64(acc + incl > u);
+      const int ll = (int)__builtin_ctzll(over);
+      int base = acc + __shfl(incl - sum, ll, 64);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int nr = __shfl(n[r], ll, 64);
+        if (u < base + nr) return UnitPos{__builtin_amdgcn_readfirstlane(cb + 4 * ll + r),
+                                          __builtin_amdgcn_readfirstlane(base)};
+        base += nr;
+      }
+    }
+    acc += chunk;
+  }
+  return UnitPos{c.B, __builtin_amdgcn_readfirstlane(acc)};
+}
+
+// Units of the sequences before b (a wavefront-wide sum; every lane returns it).
+__device__ int units_before(const CacheView& c, int b) {
+  const int lane = threadIdx.x & 63;
+  int sum = 0;
+  for (int b0 = 0; b0 < b; b0 += 256) {
+    int n[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // four loads in flight per lane
+      const int bb = b0 + lane + 64 * k;
+      n[k] = bb < b ? seq_tiles(c, bb) : 0;
+    }
+    sum += c.H * (n[0] + n[1] + n[2] + n[3]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  return __builtin_amdgcn_readfirstlane(sum);
+}
 
 template <int KB, int VB, int KAXIS, int G, bool SPARSE>
 __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, const uint16_t* __restrict__ q,
@@ -265,244 +470,271 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   constexpr int kQMinV = -(1 << (VB - 1));
   constexpr bool kPermV = VB != 8;  // k-slot pairs (i, i+4) for 4/2-bit values
   static_assert(2 * G <= 16, "hi/lo rows must fit 16");
-  // value of one code step in the key / value operands, and its inverse
-  constexpr int kShK = code_shift<KB>(), kShV = code_shift<VB>();
-  const float kUnitK = __builtin_bit_cast(float, (uint32_t)(127 - 24 + kShK) << 23);
-  const float kInvUnitK = __builtin_bit_cast(float, (uint32_t)(127 + 24 - kShK) << 23);
+  // unit of one code step in the key / value operands, and its inverse
+  constexpr int kShK = unit_shift<KB>(), kShV = unit_shift<VB>();
+  constexpr float kUnitK = pow2f(kShK - 24), kInvUnitK = pow2f(24 - kShK);
+  // The value-scale factor 2^kv, kv = kKvTop - E, is set from the largest fp16
+  // biased exponent E among the value scales seen so far, so that s * 2^kv <
+  // 2^6 and the P operand p * s * 2^kv < 2^14 stays inside fp16.
+  constexpr int kKvTop = 20;
+  constexpr _Float16 kZv = (_Float16)pow2f(kShV - 24);                // value code step
+  constexpr _Float16 kZvOfs = (_Float16)(-kQMinV * pow2f(kShV - 24));  // -q_min in code steps
 
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, c16 = lane & 15, grp = lane >> 4;
-  const int L = min(max(c.seq_len[b], 0), c.T);  // clamped: never past the capacity
-  const int nsplit_b = (L + p.tokens_per_split - 1) / p.tokens_per_split;
-  if (split > 0 && split >= nsplit_b) return;  // beyond this sequence (split 0 always runs)
-  const int Q = KAXIS ? L - L % c.R : L;
-  const int ts0 = split * p.tokens_per_split;
-  const int ts1 = min(ts0 + p.tokens_per_split, L);
-  const size_t bh = (size_t)b * c.H + h;
-  const int hq = c16 & (G - 1);           // head of this lane's column / row
-  const bool live = c16 < 2 * G;          // lanes whose column / row is used
+  const int hq = c16 % G;                         // head of this lane's column / row
+  const bool lo_col = ((c16 / G) & 1) != 0;       // column / row holds the lo part
+  const int brow = lo_col ? G + hq : hq;          // B-operand row this lane reads
+  const float rowlo = lo_col ? 1.f : 0.f;         // lo rows of P
+  const float qscale = p.scale * kLog2e;          // scores in log2 units
 
   constexpr int kWaveBytes = NB * Gm::kBytes + Gm::kWaveLds;
   constexpr int kMain = 4 * kWaveBytes;
   constexpr int kMerge = (int)sizeof(MergeLds<G>);
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMain > kMerge ? kMain : kMerge];
-  __shared__ float qsh[SPARSE ? G : 1][kD];
+  // query heads pre-scaled for the sparse entries (written identically by every wavefront)
+  __shared__ float qsh[SPARSE ? G : 1][SPARSE ? kD : 1];
 
   uint8_t* wbase = smem + w * kWaveBytes;             // this wavefront's slots
   WaveLds<G>& wl = *reinterpret_cast<WaveLds<G>*>(wbase + NB * Gm::kBytes);
   const uint32_t wbase_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)wbase;
-
-  // query heads of this KV head, pre-scaled by softmax_scale * log2(e)
-  const float qscale = p.scale * kLog2e;
-  const uint16_t* qg = q + ((size_t)b * p.Hq + (size_t)h * G) * kD;
-  if constexpr (SPARSE) {  // sparse entries add q * x directly to the scaled score
-    for (int i = tid; i < G * kD; i += 256) qsh[i / kD][i % kD] = h2f(qg[i]) * (qscale * kUnitK);
-    __syncthreads();
-  }
+  // the query heads land in the last slot, which no tile load touches before
+  // the pipeline loop starts
+  const uint32_t q_lds = wbase_lds + (NB - 1) * Gm::kBytes;
+  const uint16_t* qlds = reinterpret_cast<const uint16_t*>(wbase + (NB - 1) * Gm::kBytes);
 
   // Channel axis: this lane builds the scaled query of 2 channels, all heads:
   // k-slot pair bp of chunk bj in lane group bg, bq = lane / 4 = 4 bg + bj.
+  // The pair's codes sit at bit bsh, so its query carries 2^(kShK - bsh).
   const int bq = lane >> 2, bp = lane & 3, bg = bq >> 2, bj = bq & 3;
   const int bc0 = key_channel<KB>(bg, bj, bp, 0), bc1 = key_channel<KB>(bg, bj, bp, 1);
-  float qv0[G], qv1[G];
-  // token axis: the B operand is the raw fp16 query (exact), column n = head n mod G
-  Frag qfrag[KAXIS ? 1 : 4];
-  // rows of the key-product B operand this lane reads (the zero row when unused)
-  const int brow_hi = live ? hq : 2 * G;
-  const int brow_lo = live ? G + hq : 2 * G;
-  if constexpr (KAXIS) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      qv0[hh] = h2f(qg[hh * kD + bc0]) * qscale;
-      qv1[hh] = h2f(qg[hh * kD + bc1]) * qscale;
-    }
-    if (lane < 16) wl.qb[lane >> 2][2 * G][lane & 3] = Frag{{0u, 0u, 0u, 0u}};
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        uint32_t v = 0;
-        if (live) {
-          const int ch0 = key_channel<KB>(grp, j, pp, 0), ch1 = key_channel<KB>(grp, j, pp, 1);
-          v = (uint32_t)qg[hq * kD + ch0] | ((uint32_t)qg[hq * kD + ch1] << 16);
-        }
-        qfrag[j].p[pp] = v;
-      }
-    }
-  }
-
-  // This wavefront's tiles: k = w, w + 4, ... over [ts0, ts1).
-  const int ntiles = (ts1 - ts0 + kBlock - 1) / kBlock;
-  const int tq = (Q > ts0) ? min((Q - ts0 + kBlock - 1) / kBlock, ntiles) : 0;  // quantized tiles
-  const int nw = (w < tq) ? (tq - w + 3) / 4 : 0;                               // of them, mine
-
-  // Tile loads go through bounded descriptors over this (sequence, KV head)'s
-  // slice of each cache array, so an offset outside the slice reads zeros
-  // and never touches other memory. Byte offsets of the next tile to issue:
-  // key codes and value blocks, the tile's start plus lane * 16 (+ 1 KiB
-  // steps); metadata, each lane its 16-byte piece of one of the arrays (value
-  // scales, key scales, sparse entries; one load per array). Offsets advance
-  // by 4 tiles per issue (the wavefront takes every 4th tile).
-  const int tw0 = ts0 + w * kBlock;
-  const uint32_t Tu = (uint32_t)c.T;
-  const u32x4 rk = make_rsrc(c.k_codes + bh * c.T * (size_t)Gm::kRowK, Tu * Gm::kRowK);
-  const u32x4 rv = make_rsrc(c.v_codes + bh * (c.T / kBlock) * (size_t)Gm::kV, (Tu / kBlock) * Gm::kV);
-  const u32x4 rvm = make_rsrc(c.v_meta + bh * c.T, Tu * 4);
-  const u32x4 rkm = KAXIS ? make_rsrc(c.k_meta + bh * (c.T / kBlock) * kD, (Tu / kBlock) * kD * 4)
-                          : make_rsrc(c.k_meta + bh * c.T, Tu * 4);
-  const u32x4 rsp = SPARSE ? make_rsrc(c.k_sparse + bh * c.T * 2, Tu * 8) : rvm;
-  uint32_t koff = (uint32_t)tw0 * Gm::kRowK + lane * 16;
-  uint32_t voff = (uint32_t)(tw0 / kBlock) * Gm::kV + lane * 16;
-  // metadata lanes: 0..7 value scales, then key scales, then sparse entries
+  const int bsh = KB == 8 ? 0 : (KB == 4 ? ((bp & 1) ? 4 : 0) : (((bj & 1) && bp == 0) ? 8 : 2 * bp + 2));
+  // zero-point operand constants of the pair: -2^(bsh-24) and q_min * 2^(bsh-24)
+  const h2v zmul = h2_splat((uint16_t)(0x8000u | (1u << bsh)));
+  const h2v zofs = h2_splat((uint16_t)(0x8000u | (1u << (bsh + KB - 1))));
+  // residual keys are plain fp16: their "scale" 2^(bsh - kShK) cancels the factor
+  const uint32_t kres = (uint32_t)(15 + bsh - kShK) << 10;
+  // metadata lanes of the tile loads: 0..7 value scales, then key scales, then sparse entries
   const int mkind = lane < 8 ? 0 : (lane < 8 + Gm::kKm / 16 ? 1 : 2);
-  uint32_t moff, mstep;
-  if (mkind == 0) {
-    moff = (uint32_t)tw0 * 4 + lane * 16;
-    mstep = 4 * kBlock * 4;
-  } else if (mkind == 1) {
-    moff = (KAXIS ? (uint32_t)(tw0 / kBlock) * kD * 4 : (uint32_t)tw0 * 4) + (lane - 8) * 16;
-    mstep = KAXIS ? 4 * kD * 4 : 4 * kBlock * 4;
-  } else {
-    moff = (uint32_t)tw0 * 8 + (uint32_t)(lane - 8 - Gm::kKm / 16) * 16;
-    mstep = 4 * kBlock * 8;
-  }
 
-  // DMA of the next tile of this wavefront into slot `slot`.
-  auto issue = [&](int slot) {
-    const uint32_t lb = wbase_lds + slot * Gm::kBytes;
-#pragma unroll
-    for (int x = 0; x < Gm::kK / 1024; ++x) dma16(rk, koff + x * 1024, lb + x * 1024);
-#pragma unroll
-    for (int x = 0; x < Gm::kV / 1024; ++x) dma16(rv, voff + x * 1024, lb + Gm::kK + x * 1024);
-    const uint32_t lbm = lb + Gm::kK + Gm::kV;
-    if (mkind == 0) dma16(rvm, moff, lbm);
-    if (mkind == 1) dma16(rkm, moff, lbm);
-    if constexpr (SPARSE) {
-      if (mkind == 2 && lane < Gm::kMetaLanes) dma16(rsp, moff, lbm);
+  // this workgroup's units
+  const int nwg = gridDim.x, iwg = blockIdx.x;
+  const int64_t U = p.units;
+  const int u1 = (int)(((int64_t)iwg + 1) * U / nwg);
+  int u = (int)((int64_t)iwg * U / nwg);
+  const UnitPos pos = locate_unit(c, u);
+  int b = pos.b, base = pos.base;
+  while (u < u1 && b < c.B) {
+    // ---- the segment: tiles [k0, k1) of (sequence b, KV head h) -------------
+    const int L = seq_len_of(c, b);
+    const int Q = quant_len(c, L);
+    const int nt = units_of(c, L);  // > 0: sequences without units are skipped
+    const int rel = u - base;
+    const int h = rel / nt, k0 = rel - h * nt;
+    const int k1 = min(nt, k0 + (u1 - u));
+    // a segment that is the whole (sequence, KV head) writes the output;
+    // otherwise a partial result, numbered by the workgroup's position among
+    // those that share the (sequence, KV head)
+    const bool whole = k0 == 0 && k1 == nt;
+    const int part = iwg - wg_of_unit(base + h * nt, U, nwg);
+    const size_t bh = (size_t)b * c.H + h;
+    const int ts0 = min(k0 * kBlock, Q), ts1 = min(k1 * kBlock, Q);
+    // This wavefront's quantized tiles: k = w, w + 4, ... over [ts0, ts1).
+    const int ntiles = (ts1 - ts0 + kBlock - 1) / kBlock;
+    const int nw = (w < ntiles) ? (ntiles - w + 3) / 4 : 0;
+    // residual fp16 keys [Q, L): with the pair's last unit
+    const int nres = (k1 == nt) ? (L - Q + kBlock - 1) / kBlock : 0;
+
+    // Tile loads go through bounded descriptors over this (sequence, KV
+    // head)'s slice of each cache array, so an offset outside the slice reads
+    // zeros and never touches other memory. Byte offsets of the next tile to
+    // issue: key codes and value blocks, the tile's start plus lane * 16 (+ 1
+    // KiB steps); metadata, each lane its 16-byte piece of one of the arrays
+    // (value scales, key scales, sparse entries; one load per array). Offsets
+    // advance by 4 tiles per issue (the wavefront takes every 4th tile).
+    const int tw0 = ts0 + w * kBlock;
+    const uint32_t Tu = (uint32_t)c.T;
+    const u32x4 rk = make_rsrc(c.k_codes + bh * c.T * (size_t)Gm::kRowK, Tu * Gm::kRowK);
+    const u32x4 rv = make_rsrc(c.v_codes + bh * (c.T / kBlock) * (size_t)Gm::kV, (Tu / kBlock) * Gm::kV);
+    const u32x4 rvm = make_rsrc(c.v_meta + bh * c.T, Tu * 4);
+    const u32x4 rkm = KAXIS ? make_rsrc(c.k_meta + bh * (c.T / kBlock) * kD, (Tu / kBlock) * kD * 4)
+                            : make_rsrc(c.k_meta + bh * c.T, Tu * 4);
+    const u32x4 rsp = SPARSE ? make_rsrc(c.k_sparse + bh * c.T * 2, Tu * 8) : rvm;
+    const u32x4 rq = make_rsrc(q + ((size_t)b * p.Hq + (size_t)h * G) * kD, G * kD * 2);
+    uint32_t koff = (uint32_t)tw0 * Gm::kRowK + lane * 16;
+    uint32_t voff = (uint32_t)(tw0 / kBlock) * Gm::kV + lane * 16;
+    uint32_t moff, mstep;
+    if (mkind == 0) {
+      moff = (uint32_t)tw0 * 4 + lane * 16;
+      mstep = 4 * kBlock * 4;
+    } else if (mkind == 1) {
+      moff = (KAXIS ? (uint32_t)(tw0 / kBlock) * kD * 4 : (uint32_t)tw0 * 4) + (lane - 8) * 16;
+      mstep = KAXIS ? 4 * kD * 4 : 4 * kBlock * 4;
+    } else {
+      moff = (uint32_t)tw0 * 8 + (uint32_t)(lane - 8 - Gm::kKm / 16) * 16;
+      mstep = 4 * kBlock * 8;
     }
-    koff += 4 * Gm::kK;
-    voff += 4 * Gm::kV;
-    moff += mstep;
-  };
 
-  float m_ref = -INFINITY, l_run = 0.f;
-  int vE = 0;                       // exponent the value-scale factor is set for
-  f4v acc[8], accz = {0.f, 0.f, 0.f, 0.f};
+    // DMA of the next tile of this wavefront into slot `slot`.
+    auto issue = [&](int slot) {
+      const uint32_t lb = wbase_lds + slot * Gm::kBytes;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
-  const float rowlo = (c16 >= G && c16 < 2 * G) ? 1.f : 0.f;  // lo rows of P
-  // zero-point operands: (z - qmin) in code-step units, from the fp16 z
-  constexpr _Float16 kZk = (_Float16)((float)(1 << kShK) * kTwoM24);
-  constexpr _Float16 kZkOfs = (_Float16)(kQMinK * (float)(1 << kShK) * kTwoM24);
-  constexpr _Float16 kZv = (_Float16)((float)(1 << kShV) * kTwoM24);
-  constexpr _Float16 kZvOfs = (_Float16)(-kQMinV * (float)(1 << kShV) * kTwoM24);
-
-  // ---- scores of one tile -> online softmax -> P.V ---------------------------
-  // sc[4e + r] is the scaled score (score = sc * cs + const) of token
-  // 8grp + 4e + r; vm[i] the value meta of token 8grp + i; vcl/vch[j] the
-  // lane's value codes of channel chunk j.
-  auto softmax_pv = [&](float (&sc)[8], float cs, const uint32_t (&vm)[8], const uint32_t (&vcl)[8],
-                        const uint32_t (&vch)[8], int t0) {
-    const int nvalid = ts1 - t0;
-    if (nvalid < kBlock) {
+      for (int x = 0; x < Gm::kK / 1024; ++x) dma16(rk, koff + x * 1024, lb + x * 1024);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (8 * grp + i >= nvalid) sc[i] = -INFINITY;
-    }
-    const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    if (__builtin_amdgcn_ballot_w64(live && __builtin_fmaf(mx, cs, -m_ref) > kLazy)) {
-      const float m_new = fmaxf(m_ref, grp_max(mx * cs));
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-      float ar[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, (4 * grp + r) & (G - 1), 64);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j][r] *= ar[r];
-        accz[r] *= ar[r];
+      for (int x = 0; x < Gm::kV / 1024; ++x) dma16(rv, voff + x * 1024, lb + Gm::kK + x * 1024);
+      const uint32_t lbm = lb + Gm::kK + Gm::kV;
+      if (mkind == 0) dma16(rvm, moff, lbm);
+      if (mkind == 1) dma16(rkm, moff, lbm);
+      if constexpr (SPARSE) {
+        if (mkind == 2 && lane < Gm::kMetaLanes) dma16(rsp, moff, lbm);
       }
-      l_run *= alpha;
-      m_ref = m_new;
-    }
-    // value-scale exponent: raise it when a scale of this tile reaches 2^6 * 2^-kv
-    const uint16_t smax =
-        umax16(umax16(umax16((uint16_t)vm[0], (uint16_t)vm[1]), umax16((uint16_t)vm[2], (uint16_t)vm[3])),
-               umax16(umax16((uint16_t)vm[4], (uint16_t)vm[5]), umax16((uint16_t)vm[6], (uint16_t)vm[7])));
-    if (__builtin_amdgcn_ballot_w64(smax >= (uint16_t)((vE + 1) << 10))) {
-      uint32_t sm = smax;
-      sm = max(sm, (uint32_t)__shfl_xor((int)sm, 16, 64));
-      sm = max(sm, (uint32_t)__shfl_xor((int)sm, 32, 64));
-      const int e_new = max(vE, (int)__builtin_amdgcn_readfirstlane(sm >> 10));
-      const float f = __builtin_bit_cast(float, (uint32_t)(127 + vE - e_new) << 23);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j][r] *= f;
-        accz[r] *= f;
-      }
-      l_run *= f;
-      vE = e_new;
-    }
-    const float kvm = (float)(kKvTop - vE) - m_ref;
-    // P = p * s * 2^kv; lo rows keep p * s * 2^kv - fp16(p * s * 2^kv)
-    float a[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cs, kvm));
-      l_run += x;
-      a[i] = mul_lo(x, vm[i]);
-    }
-    Frag pf, bz;
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const int i0 = kPermV ? pp : 2 * pp;
-      const int i1 = kPermV ? pp + 4 : 2 * pp + 1;
-      const uint32_t hi = pk_rtz(a[i0], a[i1]);
-      pf.p[pp] = pk_rtz(__builtin_fmaf(f16lo(hi), -rowlo, a[i0]), __builtin_fmaf(f16hi(hi), -rowlo, a[i1]));
-      // (z'_i0, z'_i1) in code-step units, z' = z - qmin
-      bz.p[pp] = pk_fma16(perm(vm[i1], vm[i0], 0x07060302u), kZv, kZvOfs);
-    }
-    accz = mfma(pf, bz, accz);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = mfma(pf, codes8<VB>(vcl[j], vch[j], 1), acc[j]);
-  };
+      koff += 4 * Gm::kK;
+      voff += 4 * Gm::kV;
+      moff += mstep;
+    };
 
-  // the B operand of the key product for a block: scaled query (hi/lo) with
-  // the per-channel scales in the low halves of km0, km1; with_zero also
-  // writes the zero-point operand -(z - qmin) (code-step units) from their high halves
-  auto build_qb = [&](uint32_t km0, uint32_t km1, bool with_zero) {
-    wave_lds_fence();
+    // the query heads, then the first tiles
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float v0 = mul_lo(qv0[hh], km0), v1 = mul_lo(qv1[hh], km1);
-      const uint32_t hi = pk_rtz(v0, v1);
-      wl.qb[bg][hh][bj].p[bp] = hi;
-      wl.qb[bg][G + hh][bj].p[bp] = pk_rtz(__builtin_fmaf(f16lo(hi), -1.f, v0), __builtin_fmaf(f16hi(hi), -1.f, v1));
-    }
-    if (with_zero) wl.zc[bg][bj][bp] = pk_fma16(perm(km1, km0, 0x07060302u), -kZk, kZkOfs);
-    wave_lds_fence();
-  };
-
-  // ---- quantized tiles through the LDS pipeline -----------------------------
-  if (nw > 0) {
+    for (int x = 0; x < Gm::kQLoads; ++x) dma16(rq, x * 1024 + lane * 16, q_lds + x * 1024);
+    const int npro = min(NB - 1, nw);
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i)
-      if (i < nw) issue(i);
+      if (i < npro) issue(i);
+    // the query has landed once at most the tile loads issued after it remain
+    wait_vm_n<Gm::kLoads>(npro);
+    if constexpr (SPARSE) {  // sparse entries add q * x directly to the scaled score
+      for (int i = lane; i < G * kD; i += 64) qsh[i / kD][i % kD] = h2f(qlds[i]) * (qscale * kUnitK);
+    }
+    float qv0[KAXIS ? G : 1], qv1[KAXIS ? G : 1];
+    // token axis: the B operand is the raw fp16 query of head n mod G (exact);
+    // qsum_u = unit * sum_c q_c for the zero-point term
+    Frag qfrag[KAXIS ? 1 : 4];
+    float qsum_u = 0.f;
+    if constexpr (KAXIS) {
+      const float qs = qscale * (float)(1 << (kShK - bsh));
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        qv0[hh] = h2f(qlds[hh * kD + bc0]) * qs;
+        qv1[hh] = h2f(qlds[hh * kD + bc1]) * qs;
+      }
+    } else {
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const int ch0 = key_channel<KB>(grp, j, pp, 0), ch1 = key_channel<KB>(grp, j, pp, 1);
+          const uint32_t a0 = qlds[hq * kD + ch0], a1 = qlds[hq * kD + ch1];
+          qfrag[j].p[pp] = a0 | (a1 << 16);
+          sum += h2f((uint16_t)a0) + h2f((uint16_t)a1);
+        }
+      }
+      qsum_u = grp_sum(sum) * kUnitK;
+    }
+    wait_lgkm0();  // the query is in registers before its slot is reused
+    wave_lds_fence();
+
+    float m_ref = -INFINITY, l_run = 0.f;
+    int vE = 0;                       // exponent the value-scale factor is set for
+    f4v acc[8], accz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
+
+    // ---- scores of one tile -> online softmax -> P.V ---------------------------
+    // sc[4e + r] is the scaled score (log2 units = sc * cs) of token
+    // 8grp + 4e + r; vm[i] the value meta of token 8grp + i; vcl/vch[j] the
+    // lane's value code words of channel chunk j.
+    auto softmax_pv = [&](float (&sc)[8], float cs, const uint32_t (&vm)[8], const uint32_t (&vcl)[8],
+                          const uint32_t (&vch)[8], int t0, int tend) {
+      const int nvalid = tend - t0;
+      if (nvalid < kBlock) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (8 * grp + i >= nvalid) sc[i] = -INFINITY;
+      }
+      const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                             fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      if (__builtin_amdgcn_ballot_w64(__builtin_fmaf(mx, cs, -m_ref) > kLazy)) {
+        const float m_new = fmaxf(m_ref, grp_max(mx * cs));
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+        float ar[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, (4 * grp + r) % G, 64);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[j][r] *= ar[r];
+          accz[r] *= ar[r];
+        }
+        l_run *= alpha;
+        m_ref = m_new;
+      }
+      // value-scale exponent: raise it when a scale of this tile reaches 2^6 * 2^-kv
+      const uint16_t smax =
+          umax16(umax16(umax16((uint16_t)vm[0], (uint16_t)vm[1]), umax16((uint16_t)vm[2], (uint16_t)vm[3])),
+                 umax16(umax16((uint16_t)vm[4], (uint16_t)vm[5]), umax16((uint16_t)vm[6], (uint16_t)vm[7])));
+      if (__builtin_amdgcn_ballot_w64(smax >= (uint16_t)((vE + 1) << 10))) {
+        uint32_t sm = smax;
+        sm = max(sm, (uint32_t)__shfl_xor((int)sm, 16, 64));
+        sm = max(sm, (uint32_t)__shfl_xor((int)sm, 32, 64));
+        const int e_new = max(vE, (int)__builtin_amdgcn_readfirstlane(sm >> 10));
+        const float f = __builtin_bit_cast(float, (uint32_t)(127 + vE - e_new) << 23);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[j][r] *= f;
+          accz[r] *= f;
+        }
+        l_run *= f;
+        vE = e_new;
+      }
+      const float kvm = (float)(kKvTop - vE) - m_ref;
+      // P = p * s * 2^kv; lo rows keep P - fp16(P)
+      float a[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cs, kvm));
+        l_run += x;
+        a[i] = mul_lo(x, vm[i]);
+      }
+      Frag pf, bz;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int i0 = kPermV ? pp : 2 * pp;
+        const int i1 = kPermV ? pp + 4 : 2 * pp + 1;
+        const uint32_t hi = pk_rtz(a[i0], a[i1]);
+        pf.p[pp] = pk_rtz(__builtin_fmaf(f16lo(hi), -rowlo, a[i0]), __builtin_fmaf(f16hi(hi), -rowlo, a[i1]));
+        // (z'_i0, z'_i1) in code steps, z' = z - qmin
+        bz.p[pp] = pk_fma16(perm(vm[i1], vm[i0], 0x07060302u), h2v{kZv, kZv}, h2v{kZvOfs, kZvOfs});
+      }
+      accz = mfma(pf, bz, accz);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = mfma(pf, val_frag<VB>(vcl[j], vch[j]), acc[j]);
+    };
+
+    // the B operand of the key product for a block: scaled query (hi/lo) with
+    // the per-channel scales in the low halves of km0, km1; with_zero also
+    // writes the zero-point operand -(z - qmin) from their high halves
+    auto build_qb = [&](uint32_t km0, uint32_t km1, bool with_zero) {
+      wave_lds_fence();
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float v0 = mul_lo(qv0[hh], km0), v1 = mul_lo(qv1[hh], km1);
+        const uint32_t hi = pk_rtz(v0, v1);
+        wl.qb[bg][hh][bj].p[bp] = hi;
+        wl.qb[bg][G + hh][bj].p[bp] = pk_rtz(__builtin_fmaf(f16lo(hi), -1.f, v0), __builtin_fmaf(f16hi(hi), -1.f, v1));
+      }
+      if (with_zero) wl.zc[bg][bj][bp] = pk_fma16(perm(km1, km0, 0x07060302u), zmul, zofs);
+      wave_lds_fence();
+    };
+
+    // ---- quantized tiles through the LDS pipeline -----------------------------
     for (int i = 0; i < nw; ++i) {
       const int slot = i % NB;
       if (i + NB - 1 < nw) issue((i + NB - 1) % NB);
       // tile i has landed once at most (tiles issued after it) x loads remain
-      switch (min(NB - 1, nw - 1 - i)) {
-        case 0: wait_vm<0>(); break;
-        case 1: wait_vm<Gm::kLoads>(); break;
-        case 2: wait_vm<(NB > 2 ? 2 : 1) * Gm::kLoads>(); break;
-        default: wait_vm<(NB > 3 ? 3 : 1) * Gm::kLoads>(); break;
-      }
+      wait_vm_n<Gm::kLoads>(min(NB - 1, nw - 1 - i));
       const uint8_t* sb = wbase + slot * Gm::kBytes;
       const uint8_t* kbuf = sb;
       const uint8_t* vbuf = sb + Gm::kK;
@@ -530,11 +762,6 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           kc[e][x + 1] = y.y;
         }
       }
-      auto key_frag = [&](int e, int j) -> Frag {
-        if constexpr (KB == 4) return codes8<4>(kc[e][j], 0u, 0);
-        else if constexpr (KB == 8) return codes8<8>(kc[e][2 * j], kc[e][2 * j + 1], 0);
-        else return codes8<2>(kc[e][j >> 1], 0u, j & 1);
-      };
       float sc[8];
       float cs;
       if constexpr (KAXIS) {
@@ -542,27 +769,18 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
         // zero-point term, the same for every token of the block
         f4v cz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const Frag az = *reinterpret_cast<const Frag*>(wl.zc[grp][j]);
-          cz = mfma(az, wl.qb[grp][brow_hi][j], cz);
-          cz = mfma(az, wl.qb[grp][brow_lo][j], cz);
-        }
+        for (int j = 0; j < 4; ++j) cz = mfma(*reinterpret_cast<const Frag*>(wl.zc[grp][j]), wl.qb[grp][brow][j], cz);
         f4v s[2] = {cz, cz};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const Frag qh = wl.qb[grp][brow_hi][j];
-          const Frag ql = wl.qb[grp][brow_lo][j];
+          const Frag qf = wl.qb[grp][brow][j];
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const Frag kf = key_frag(e, j);
-            s[e] = mfma(kf, qh, s[e]);
-            s[e] = mfma(kf, ql, s[e]);
-          }
+          for (int e = 0; e < 2; ++e) s[e] = mfma(key_frag<KB, false>(kc[e], j), qf, s[e]);
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sc[4 * e + r] = s[e][r];
+          for (int r = 0; r < 4; ++r) sc[4 * e + r] = add_ror<G>(s[e][r]);
         cs = kInvUnitK;
       } else {
         uint32_t km[8];
@@ -572,23 +790,20 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           km[0] = a.x; km[1] = a.y; km[2] = a.z; km[3] = a.w;
           km[4] = bb.x; km[5] = bb.y; km[6] = bb.z; km[7] = bb.w;
         }
-        f4v s[2];
+        const float seed = (float)kQMinK * qsum_u;  // sum_c q_c (u_c + q_min) = sum_c q_c q_c'
+        f4v s[2] = {f4v{seed, seed, seed, seed}, f4v{seed, seed, seed, seed}};
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          // zero-point term of the row's token: -(z - qmin) * sum_c q_c
-          const uint32_t ka = kmeta[a_token(e, c16)];
-          const uint32_t az1 = pk_fma16(perm(ka, ka, 0x07060706u), -kZk, kZkOfs);
-          const Frag az = {{az1, az1, az1, az1}};
-          s[e] = f4v{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) s[e] = mfma(az, qfrag[j], s[e]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) s[e] = mfma(key_frag(e, j), qfrag[j], s[e]);
-        }
+          for (int e = 0; e < 2; ++e) s[e] = mfma(key_frag<KB, true>(kc[e], j), qfrag[j], s[e]);
+        // minus z_t * sum_c q_c, then times the token's scale
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sc[4 * e + r] = mul_lo(s[e][r], km[4 * e + r]);
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t kw = km[4 * e + r];
+            sc[4 * e + r] = mul_lo(__builtin_fmaf(f16hi(kw), -qsum_u, s[e][r]), kw);
+          }
         cs = kInvUnitK * qscale;
       }
       if constexpr (SPARSE) {
@@ -601,152 +816,196 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
       // value codes: channel 16j + c16, tokens 8grp .. 8grp+7 of the block
       uint32_t vcl[8], vch[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint8_t* rec = vbuf + (16 * j + c16) * 4 * VB;
-        if constexpr (VB == 4) {
-          vcl[j] = reinterpret_cast<const uint32_t*>(rec)[grp];
-          vch[j] = 0u;
-        } else if constexpr (VB == 8) {
-          const uint2 x = reinterpret_cast<const uint2*>(rec)[grp];
-          vcl[j] = x.x;
-          vch[j] = x.y;
-        } else {
-          // 8 two-bit fields -> byte 1 (tokens 0..3) and byte 3 (tokens 4..7)
-          vcl[j] = perm(0u, reinterpret_cast<const uint16_t*>(rec)[grp], 0x010C000Cu);
-          vch[j] = 0u;
-        }
-      }
-      softmax_pv(sc, cs, vm, vcl, vch, t0);
+      for (int j = 0; j < 8; ++j) val_words<VB>(vbuf + (16 * j + c16) * 4 * VB, grp, vcl[j], vch[j]);
+      softmax_pv(sc, cs, vm, vcl, vch, t0, ts1);
     }
-  }
 
-  // ---- residual (fp16) key tiles: channel axis only ------------------------
-  if constexpr (KAXIS) {
-    for (int k = tq + ((w - tq) % 4 + 4) % 4; k < ntiles; k += 4) {
-      const int t0 = ts0 + k * kBlock;
-      uint32_t vm[8], vcl[8], vch[8];
-      {
-        const uint8_t* vblk = c.v_codes + (bh * (c.T / kBlock) + t0 / kBlock) * (size_t)Gm::kV;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint8_t* rec = vblk + (16 * j + c16) * 4 * VB;
-          if constexpr (VB == 4) { vcl[j] = reinterpret_cast<const uint32_t*>(rec)[grp]; vch[j] = 0u; }
-          else if constexpr (VB == 8) {
-            const uint2 x = reinterpret_cast<const uint2*>(rec)[grp];
-            vcl[j] = x.x; vch[j] = x.y;
-          } else {
-            vcl[j] = perm(0u, reinterpret_cast<const uint16_t*>(rec)[grp], 0x010C000Cu);
-            vch[j] = 0u;
-          }
-        }
-        const uint4* vmg = reinterpret_cast<const uint4*>(c.v_meta + bh * c.T + t0 + 8 * grp);
-        const uint4 a = vmg[0], bb = vmg[1];
-        vm[0] = a.x; vm[1] = a.y; vm[2] = a.z; vm[3] = a.w;
-        vm[4] = bb.x; vm[5] = bb.y; vm[6] = bb.z; vm[7] = bb.w;
-      }
-      // B operand: query scaled by the softmax factor only (scale 1.0), hi/lo
-      build_qb(0x3C00u, 0x3C00u, false);
-      f4v s[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int tt = t0 + a_token(e, c16);
-        const bool ok = tt < ts1;
-        // the lane group's 32 fp16 keys, channels 32grp .. 32grp+31
-        const uint4* kr = reinterpret_cast<const uint4*>(c.k_resid + (bh * c.R + (ok ? tt - Q : 0)) * kD + 32 * grp);
-        uint32_t rw[16];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          uint4 v = kr[x];
-          if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
-          rw[4 * x] = v.x; rw[4 * x + 1] = v.y; rw[4 * x + 2] = v.z; rw[4 * x + 3] = v.w;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // k-slot pair pp of chunk j: the keys of the channels the codes use
-          Frag kf;
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {
-            const int c0 = key_channel<KB>(0, j, pp, 0), c1 = key_channel<KB>(0, j, pp, 1);
-            const uint32_t sel = ((c0 & 1) ? 0x0302u : 0x0100u) | ((c1 & 1) ? 0x07060000u : 0x05040000u);
-            kf.p[pp] = perm(rw[c1 >> 1], rw[c0 >> 1], sel);
-          }
-          s[e] = mfma(kf, wl.qb[grp][brow_hi][j], s[e]);
-          s[e] = mfma(kf, wl.qb[grp][brow_lo][j], s[e]);
-        }
-      }
-      float sc[8];
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[4 * e + r] = s[e][r] * kUnitK;
-      softmax_pv(sc, kInvUnitK, vm, vcl, vch, t0);
-    }
-  }
 
-  // ---- merge the wavefronts of the workgroup --------------------------------
-  // o = (acc - accz) / (value code step) * 2^-kv, l = l_run * 2^-kv
-  const float ofac = __builtin_bit_cast(float, (uint32_t)(127 + 24 - kShV - kKvTop + vE) << 23);
-  const float lfac = __builtin_bit_cast(float, (uint32_t)(127 - kKvTop + vE) << 23);
-  const float lsum = grp_sum(l_run) * lfac;
-  __syncthreads();  // every wavefront is done with its slots
-  MergeLds<G>& mg = *reinterpret_cast<MergeLds<G>*>(smem);
-  if (grp == 0 && c16 < G) {
-    mg.m[w][c16] = m_ref;
-    mg.l[w][c16] = lsum;
-  }
+    // ---- residual (fp16) key tiles, channel axis only: tile j holds tokens
+    // Q + 32 j .. + 31 (< L); this wavefront takes j = w, w + 4, ... They go
+    // through the wavefront's LDS slots, free after the pipeline: the value
+    // block and value scales as for a code tile, and the fp16 keys 16 tokens
+    // (one A-row block, 4 KiB) at a time; each half runs the key product, the
+    // softmax and P.V of its 16 tokens (the other half's scores masked).
+    if constexpr (KAXIS) {
+      const uint32_t lk = wbase_lds, lv = wbase_lds + 4096, lm = lv + Gm::kV;
+      const uint8_t* kres_lds = wbase;
+      const uint8_t* vres_lds = wbase + 4096;
+      const uint32_t* vmres_lds = reinterpret_cast<const uint32_t*>(wbase + 4096 + Gm::kV);
+      const u32x4 rr = make_rsrc(c.k_resid + bh * c.R * (size_t)kD, (uint32_t)c.R * kD * 2);
+      for (int jr = w; jr < nres; jr += 4) {
+        const int t0 = Q + jr * kBlock;
+        wait_lgkm0();  // earlier LDS reads of the slots are done
+        wave_lds_fence();
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+        for (int x = 0; x < Gm::kV / 1024; ++x)
+          dma16(rv, (uint32_t)(t0 / kBlock) * Gm::kV + x * 1024 + lane * 16, lv + x * 1024);
+        if (lane < 8) dma16(rvm, (uint32_t)t0 * 4 + lane * 16, lm);
+        // B operand: query scaled by the softmax factor only (the pair's 2^lf
+        // cancelled), hi/lo
+        build_qb(kres, kres, false);
+#pragma nounroll
+        for (int e = 0; e < 2; ++e) {
+          // keys of row block e: LDS row m (0..15) = token t0 + a_token(e, m);
+          // each load moves 4 rows, lane l a 16-byte piece of row 4x + l/16
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * grp + r;
-      if (row < 2 * G) mg.o[w][row][16 * j + c16] = (acc[j][r] - accz[r]) * ofac;
-    }
-  __syncthreads();
-  const bool single = nsplit_b <= 1;
-  for (int e = tid; e < G * kD; e += 256) {
-    const int hh = e / kD, ch = e % kD;
-    float M = mg.m[0][hh];
+          for (int x = 0; x < 4; ++x) {
+            const int tt = t0 - Q + a_token(e, 4 * x + (lane >> 4));
+            dma16(rr, (uint32_t)tt * (kD * 2) + (lane & 15) * 16, lk + x * 1024);
+          }
+          wait_vm<0>();
+          uint32_t rk[16];
+          {
+            const uint4* kr4 = reinterpret_cast<const uint4*>(kres_lds + c16 * (kD * 2) + grp * 64);
 #pragma unroll
-    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, mg.m[ww][hh]);
-    float o = 0.f, l = 0.f;
-    if (M != -INFINITY) {
+            for (int x = 0; x < 4; ++x) {
+              const uint4 v = kr4[x];
+              rk[4 * x] = v.x; rk[4 * x + 1] = v.y; rk[4 * x + 2] = v.z; rk[4 * x + 3] = v.w;
+            }
+          }
+          f4v s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        const float f = __builtin_amdgcn_exp2f(mg.m[ww][hh] - M);
-        o += f * (mg.o[ww][hh][ch] + mg.o[ww][G + hh][ch]);
-        l += f * mg.l[ww][hh];
+          for (int j = 0; j < 4; ++j) {
+            // k-slot pair pp of chunk j: the keys of the channels the codes use
+            Frag kf;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+              const int c0 = key_channel<KB>(0, j, pp, 0), c1 = key_channel<KB>(0, j, pp, 1);
+              const uint32_t sel = ((c0 & 1) ? 0x0302u : 0x0100u) | ((c1 & 1) ? 0x07060000u : 0x05040000u);
+              kf.p[pp] = perm(rk[c1 >> 1], rk[c0 >> 1], sel);
+            }
+            s1 = mfma(kf, wl.qb[grp][brow][j], s1);
+          }
+          float sc[8];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {  // tokens 8grp + 4e + r: slots 4e + r
+            const float v = add_ror<G>(s1[r]);
+            sc[r] = (e == 0) ? v : -INFINITY;
+            sc[4 + r] = (e == 0) ? -INFINITY : v;
+          }
+          uint32_t vm[8], vcl[8], vch[8];
+          {
+            const uint4 a = reinterpret_cast<const uint4*>(vmres_lds + 8 * grp)[0];
+            const uint4 bb = reinterpret_cast<const uint4*>(vmres_lds + 8 * grp)[1];
+            vm[0] = a.x; vm[1] = a.y; vm[2] = a.z; vm[3] = a.w;
+            vm[4] = bb.x; vm[5] = bb.y; vm[6] = bb.z; vm[7] = bb.w;
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) val_words<VB>(vres_lds + (16 * j + c16) * 4 * VB, grp, vcl[j], vch[j]);
+          softmax_pv(sc, 1.f, vm, vcl, vch, t0, L);
+          wait_lgkm0();  // the keys are read before the next half's loads
+          wave_lds_fence();
+        }
       }
     }
-    const size_t qh = (size_t)b * p.Hq + (size_t)h * G + hh;
-    if (single) {
-      out[qh * kD + ch] = (l > 0.f) ? o / l : 0.f;
-    } else {
-      float* part = ws + (qh * p.n_split + split) * kPartialFloats;
-      if (ch == 0) { part[0] = M; part[1] = l; }
-      part[4 + ch] = o;
+
+    // ---- merge the wavefronts of the workgroup ------------------------------
+    // o = (acc - accz) / (value code unit) * 2^-kv, l = l_run * 2^-kv
+    const float ofac = __builtin_bit_cast(float, (uint32_t)(127 + 24 - kShV - kKvTop + vE) << 23);
+    const float lfac = __builtin_bit_cast(float, (uint32_t)(127 - kKvTop + vE) << 23);
+    const float lsum = grp_sum(l_run) * lfac;
+    wait_vm<0>();     // no tile load still writing LDS
+    __syncthreads();  // every wavefront is done with its slots
+    MergeLds<G>& mg = *reinterpret_cast<MergeLds<G>*>(smem);
+    if (grp == 0 && c16 < G) {
+      mg.m[w][c16] = m_ref;
+      mg.l[w][c16] = lsum;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * grp + r;
+        if (row < 2 * G) mg.o[w][row][16 * j + c16] = (acc[j][r] - accz[r]) * ofac;
+      }
+    __syncthreads();
+    for (int e = tid; e < G * kD; e += 256) {
+      const int hh = e / kD, ch = e % kD;
+      float M = mg.m[0][hh];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, mg.m[ww][hh]);
+      float o = 0.f, l = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const float f = __builtin_amdgcn_exp2f(mg.m[ww][hh] - M);
+          o += f * (mg.o[ww][hh][ch] + mg.o[ww][G + hh][ch]);
+          l += f * mg.l[ww][hh];
+        }
+      }
+      const size_t qh = (size_t)b * p.Hq + (size_t)h * G + hh;
+      if (whole) {
+        out[qh * kD + ch] = (l > 0.f) ? o / l : 0.f;
+      } else {
+        float* pt = ws + (qh * p.max_parts + part) * kPartialFloats;
+        if (ch == 0) { pt[0] = M; pt[1] = l; }
+        pt[4 + ch] = o;
+      }
+    }
+    __syncthreads();  // the merge area is free again before the next segment's loads
+
+    // ---- next segment -------------------------------------------------------
+    u += k1 - k0;
+    if (k1 == nt && h == c.H - 1) {
+      base += c.H * nt;
+      ++b;
+      while (b < c.B && seq_tiles(c, b) == 0) ++b;
     }
   }
 }
 
-// Log-sum-exp merge of the split partials of sequences that were split: one
-// workgroup per (sequence, query head), one thread per channel.
+// Merge kernel: one workgroup of 128 threads (one per channel) per
+// (sequence, query head) whose output the attention kernel did not write:
+// sequences with no tokens (output 0) and pairs whose units span several
+// workgroups, whose partial results it merges with a log-sum-exp. The
+// partials' (m, l) are staged in LDS by one parallel load; their outputs are
+// loaded 8 at a time.
 __global__ __launch_bounds__(128) void combine_kernel(CacheView c, AttnPlan p, const float* __restrict__ ws,
                                                       float* __restrict__ out) {
+  constexpr int kBatch = 128;  // partials staged at a time
+  __shared__ float pml[kBatch][2];
   const int bq = blockIdx.x, ch = threadIdx.x;
-  const int b = bq / p.Hq;
-  const int L = min(max(c.seq_len[b], 0), c.T);  // clamped: never past the capacity
-  const int ns = (L + p.tokens_per_split - 1) / p.tokens_per_split;
-  if (ns <= 1) return;  // written directly by the attention kernel
-  const float* part = ws + (size_t)bq * p.n_split * kPartialFloats;
-  float M = -INFINITY;
-  for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, part[s2 * kPartialFloats]);
-  float o = 0.f, l = 0.f;
-  if (M != -INFINITY) {
-    for (int s2 = 0; s2 < ns; ++s2) {
-      const float f = __builtin_amdgcn_exp2f(part[s2 * kPartialFloats] - M);
-      o += f * part[s2 * kPartialFloats + 4 + ch];
-      l += f * part[s2 * kPartialFloats + 1];
+  const int b = bq / p.Hq, hkv = (bq % p.Hq) / p.group;
+  const int L = seq_len_of(c, b);
+  if (L == 0) {
+    out[(size_t)bq * kD + ch] = 0.f;
+    return;
+  }
+  const int nt = units_of(c, L);
+  const int s0 = units_before(c, b) + hkv * nt;  // the pair's units [s0, s0 + nt)
+  const int np = min(wg_of_unit(s0 + nt - 1, p.units, p.n_wg) - wg_of_unit(s0, p.units, p.n_wg) + 1, p.max_parts);
+  if (np <= 1) return;  // written by the attention kernel
+  const float* part = ws + (size_t)bq * p.max_parts * kPartialFloats;
+  float M = -INFINITY, o = 0.f, l = 0.f;
+  for (int j0 = 0; j0 < np; j0 += kBatch) {
+    const int n = min(kBatch, np - j0);
+    __syncthreads();
+    if (ch < n) {
+      pml[ch][0] = part[(j0 + ch) * kPartialFloats];
+      pml[ch][1] = part[(j0 + ch) * kPartialFloats + 1];
     }
+    __syncthreads();
+    float mb = -INFINITY;
+    for (int j = 0; j < n; ++j) mb = fmaxf(mb, pml[j][0]);
+    const float m_new = fmaxf(M, mb);
+    if (m_new == -INFINITY) continue;
+    const float fo = __builtin_amdgcn_exp2f(M - m_new);
+    o *= fo;
+    l *= fo;
+    for (int j = 0; j < n; j += 8) {
+      float ov[8];
+#pragma unroll
+      for (int y = 0; y < 8; ++y) ov[y] = (j + y < n) ? part[(j0 + j + y) * kPartialFloats + 4 + ch] : 0.f;
+#pragma unroll
+      for (int y = 0; y < 8; ++y) {
+        if (j + y < n) {
+          const float f = __builtin_amdgcn_exp2f(pml[j + y][0] - m_new);
+          o = __builtin_fmaf(f, ov[y], o);
+          l = __builtin_fmaf(f, pml[j + y][1], l);
+        }
+      }
+    }
+    M = m_new;
   }
   out[(size_t)bq * kD + ch] = (l > 0.f) ? o / l : 0.f;
 }
@@ -776,7 +1035,7 @@ hipError_t launch_t(const CacheView& c, const AttnPlan& p, const uint16_t* q, fl
     *occ = std::max(1, std::min(std::min(by_vgpr, by_lds), 8));
     return hipSuccess;
   }
-  dim3 grid(p.n_split, c.H, c.B);
+  dim3 grid(p.n_wg);
   hipLaunchKernelGGL((attn_kernel<KB, VB, KAXIS, G, SPARSE>), grid, dim3(256), 0, st, c, p, q, out, ws);
   return hipGetLastError();
 }
@@ -826,8 +1085,11 @@ hipError_t dispatch(const CacheView& c, const AttnPlan& p, const uint16_t* q, fl
 
 hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out,
                                    float* ws, hipStream_t st) {
-  const hipError_t e = dispatch(c, p, q, out, ws, st, nullptr);
-  if (e != hipSuccess || p.n_split <= 1) return e;
+  if (p.n_wg > 0) {
+    const hipError_t e = dispatch(c, p, q, out, ws, st, nullptr);
+    if (e != hipSuccess) return e;
+  }
+  if (!p.need_combine) return hipSuccess;
   hipLaunchKernelGGL(combine_kernel, dim3(c.B * p.Hq), dim3(kD), 0, st, c, p, ws, out);
   return hipGetLastError();
 }

@@ -49,9 +49,11 @@ hipError_t launch_dequantize(const CacheView& c, uint16_t* k_out,
 
 struct AttnPlan {
   int Hq, group;               // query heads, query heads per KV head
-  int n_split;                 // splits per (sequence, KV head)
-  int tokens_per_split;        // multiple of 32
   float scale;                 // softmax scale
+  int64_t units;               // 32-token tiles of all (sequence, KV head) pairs
+  int n_wg;                    // attention workgroups (each takes units / n_wg)
+  int max_parts;               // partial-result slots per (sequence, query head)
+  int need_combine;            // some pair spans several workgroups, or a sequence is empty
 };
 hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p,
                                    const uint16_t* q, float* out, float* ws,
@@ -60,14 +62,14 @@ hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p,
 // compute unit (at least 1).
 int attention_blocks_per_cu(const CacheView& c, int group);
 
-// Workspace: fp32 partials [B][Hq][n_split][kPartialFloats] = m, l, 2 pad,
-// o[128].
+// Workspace: fp32 partials [B][Hq][max_parts][kPartialFloats] = m, l, 2 pad,
+// o[128]. Every workgroup takes at least kMinUnitsPerWg tiles, so the tiles of
+// one (sequence, KV head), at most T/32, meet at most T/32/kMinUnitsPerWg + 2
+// workgroup ranges.
 constexpr int kPartialFloats = 4 + kD;
-constexpr int kMinSplitTokens = 256;
-constexpr int kMinSplitTiles = kMinSplitTokens / kBlock;
-// Upper bound on splits per (sequence, KV head) for a given capacity.
-inline int max_splits_for(int max_tokens) {
-  return (max_tokens + kMinSplitTokens - 1) / kMinSplitTokens;
+constexpr int kMinUnitsPerWg = 8;
+inline int max_parts_for(int max_tokens) {
+  return (max_tokens / kBlock + kMinUnitsPerWg - 1) / kMinUnitsPerWg + 2;
 }
 
 }  // namespace kvq

@@ -153,9 +153,10 @@ def test_workspace_shared_by_two_caches():
 
 
 def test_split_length_varied_on_one_input(monkeypatch):
-    """The same cache and queries attended with split lengths from the
-    shortest allowed (256 tokens, up to 5 splits here) to one split per
-    sequence: every result within 2e-3 of the oracle, and of each other."""
+    """The same cache and queries attended with the work cut into ranges of
+    8 tiles (256 tokens, the shortest allowed: pairs split over up to 5
+    workgroups here) up to a single workgroup for everything: every result
+    within 2e-3 of the oracle, and of each other."""
     s = W.spec(2, batch=3, seq_len=1200, min_len=900)
     k, v, lens = prefill_inputs(s, 0)
     p = Pair(s, s.max_tokens(8))
