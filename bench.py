@@ -9,12 +9,19 @@ in every layer of the workload (the 32-layer worked-example shape runs all
 Inputs are resident in HBM before timing starts. Cache replicas are rotated so
 each step reads a cache that is not resident in the 256 MB last-level cache.
 
-Prints one JSON line: tokens/s (value), ms per step, and for the attention
-kernel a roofline entry (algorithmic bytes per launch / measured launch time
-against 8 TB/s HBM) plus the float64 oracle timed on the host as a reported
-baseline. An "append" entry reports the quantize-on-append path on its own:
-a whole-context prefill (GB/s over its algorithmic bytes) and the per-step
-append of one token per sequence.
+By default the int4 and int2 KIVI workloads (2 and 4) and the ragged int4 +
+sparse streaming workload (5) run in turn; the JSON line's headline fields
+(value, ms_per_step, config, roofline) are workload 5's, the largest, and a
+"workloads" array carries each one's figures. --config N runs one workload.
+
+For each workload: tokens/s over the whole decode step, ms per step, and for
+the attention call a roofline entry (algorithmic bytes per launch / measured
+launch time against 8 TB/s HBM, with the HBM traffic recorded by rocprofv3
+counters when they were taken on the current kernel sources), plus an "append"
+entry for the quantize-on-append path on its own: a whole-context prefill (GB/s
+over its algorithmic bytes) and the per-step append of one token per sequence.
+The float64 oracle is timed on the host on a bounded sample of the headline
+workload as a reported baseline.
 """
 import argparse
 import json
@@ -103,29 +110,57 @@ def append_report(s, lens, prefill_ms, step_ms):
             "decode_step_append_us": float(np.mean(step_ms)) * 1e3}
 
 
+def host_cpu():
+    """(usable cores, CPU model) of the host this process runs on."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
 def cpu_baseline(s, n_seq, steps):
-    """The oracle's decode step (append + float64 attention) on a subset of the
-    sequences, timed on the host. Returns (tokens/s, threads, description)."""
+    """The oracle's decode step (append + float64 attention) on the n_seq
+    sequences closest to the median length, timed on the host with numpy's
+    BLAS pool held to one thread. Returns (tokens/s, seconds, the sample's
+    lengths)."""
     from dataclasses import replace
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
     from oracle.cache import Config as RC, RefCache
     from quantized_decode_attention_03_amd import workloads as W
-    sub = replace(s, batch=n_seq)
-    lens = [int(x) for x in W.seq_lengths(s)[:n_seq]]
-    ref = RefCache(RC(s.d_head, s.n_kv_heads, s.n_q_heads, s.k_bits, s.v_bits, s.k_axis,
-                      s.k_group, s.k_residual, s.k_sparse), n_seq,
-                   ((max(lens) + steps + 31) // 32) * 32)
-    ks, vs = zip(*[W.prefill(s, 0, b, lens[b]) for b in range(n_seq)])
-    ref.append(np.concatenate(ks), np.concatenate(vs), lens)
-    scale = 1.0 / math.sqrt(s.d_head)
-    inputs = [W.step(sub, 0, i) for i in range(steps)]
-    t0 = time.perf_counter()
-    for q, kn, vn in inputs:
-        ref.append(kn, vn, [1] * n_seq)
-        ref.attention(q, scale)
-    dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return n_seq * steps / dt, threads, dt
+    lens_all = [int(x) for x in W.seq_lengths(s)]
+    order = sorted(range(s.batch), key=lambda b: lens_all[b])
+    lo = max(0, min(len(order) - n_seq, len(order) // 2 - n_seq // 2))
+    pick = sorted(order[lo:lo + n_seq])
+    lens = [lens_all[b] for b in pick]
+    sub = replace(s, batch=len(pick))
+    with threadpool_limits(1):
+        ref = RefCache(RC(s.d_head, s.n_kv_heads, s.n_q_heads, s.k_bits, s.v_bits, s.k_axis,
+                          s.k_group, s.k_residual, s.k_sparse), len(pick),
+                       ((max(lens) + steps + 31) // 32) * 32)
+        ks, vs = zip(*[W.prefill(s, 0, b, lens_all[b]) for b in pick])
+        ref.append(np.concatenate(ks), np.concatenate(vs), lens)
+        scale = 1.0 / math.sqrt(s.d_head)
+        inputs = []
+        for i in range(steps):
+            q, kn, vn = W.step(s, 0, i)
+            inputs.append((q[pick], kn[pick], vn[pick]))
+        t0 = time.perf_counter()
+        for q, kn, vn in inputs:
+            ref.append(kn, vn, [1] * len(pick))
+            ref.attention(q, scale)
+        dt = time.perf_counter() - t0
+    del sub
+    return len(pick) * steps / dt, dt, lens
 
 
 def copy_probe():
@@ -151,38 +186,17 @@ def copy_probe():
                       "read_plus_write_GBps": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..5")
-    ap.add_argument("--replicas", type=int, default=0, help="cache copies rotated (0: auto)")
-    ap.add_argument("--settle-ms", type=float, default=300.0,
-                    help="untimed attention launches before the warmup steps (device clock ramp)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=16)
-    ap.add_argument("--cpu-steps", type=int, default=8)
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="time a plain 1 GiB device copy (HBM reference and counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the decode path shards by sequence or KV head with no communication, "
-              "so one GPU's throughput is the per-GPU figure)", file=sys.stderr)
-        sys.exit(2)
+DEFAULT_WORKLOADS = (2, 4, 5)   # int4 KIVI, int2 KIVI, ragged int4 + sparse (headline: the largest)
 
+
+def run_workload(cid, args):
+    """Prefill, settle, warm up and time one workload; returns its result
+    entry (everything but the host baseline)."""
     import torch
     import quantized_decode_attention_03_amd as K
     from quantized_decode_attention_03_amd import workloads as W
-    from quantized_decode_attention_03_amd import _native
 
-    _native.lib()
-    if args.copy_probe:
-        copy_probe()
-        return
-    s = W.spec(args.config)
-    torch.cuda.set_device(0)
+    s = W.spec(cid)
     dev = "cuda"
     lens0 = [int(x) for x in W.seq_lengths(s)]
     cache_bytes = algorithmic_bytes(s, lens0)
@@ -312,45 +326,99 @@ def main():
     attn_avg_s = float(np.mean(attn_ms)) / 1e3
     bytes_avg = float(np.mean([algorithmic_bytes(s, L) for L in lens_timed]))
     achieved = bytes_avg / attn_avg_s / 1e9
-
-    progress(f"{args.steps} timed steps in {wall:.3f} s")
-    ms_per_step = wall / args.steps * 1e3
-    value = s.batch * args.steps / wall
-    res = {
-        "metric": METRIC,
-        "value": value,
+    progress(f"workload {s.cid}: {args.steps} timed steps in {wall:.3f} s, attention {attn_avg_s * 1e6:.1f} us")
+    return {
+        "workload": s.name,
+        "value": s.batch * args.steps / wall,
         "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "ms_per_step": wall / args.steps * 1e3,
         "dtype": f"f16 MFMA, f32 accumulate (int{s.k_bits}/int{s.v_bits} codes)",
-        "data": "synthetic",
         "config": {"workload": s.name, "batch": s.batch, "n_q_heads": s.n_q_heads,
                    "n_kv_heads": s.n_kv_heads, "d_head": s.d_head, "seq_len": s.seq_len,
-                   "k_bits": s.k_bits, "v_bits": s.v_bits, "k_axis": s.k_axis,
-                   "k_group": s.k_group, "k_residual": s.k_residual, "k_sparse": s.k_sparse,
-                   "layers": nlay, "cache_replicas": nrep},
+                   "min_len": s.min_len, "k_bits": s.k_bits, "v_bits": s.v_bits,
+                   "k_axis": s.k_axis, "k_group": s.k_group, "k_residual": s.k_residual,
+                   "k_sparse": s.k_sparse, "layers": nlay, "cache_replicas": nrep},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_GBS, "traffic": recorded_traffic(args.config),
-                     "kernel": "kvq_decode_attention (attention + split merge)",
+                     "frac": achieved / PEAK_GBS, "traffic": recorded_traffic(s.cid),
+                     "kernel": "kvq_decode_attention (attention kernel + partial merge)",
                      "avg_launch_us": attn_avg_s * 1e6,
                      "p10_p90_us": [float(np.percentile(attn_ms, 10)) * 1e3,
                                     float(np.percentile(attn_ms, 90)) * 1e3],
                      "algorithmic_bytes_per_launch": bytes_avg},
         "append": append_report(s, lens0, prefill_ms, append_ms),
     }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=0,
+                    help="one workload 1..5 (default: workloads 2, 4 and 5, headline 5)")
+    ap.add_argument("--replicas", type=int, default=0, help="cache copies rotated (0: auto)")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed attention launches before the warmup steps (device clock ramp)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=4)
+    ap.add_argument("--cpu-steps", type=int, default=4)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="time a plain 1 GiB device copy (HBM reference and counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path shards by sequence or KV head with no communication, "
+              "so one GPU's throughput is the per-GPU figure)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_decode_attention_03_amd import workloads as W
+    from quantized_decode_attention_03_amd import _native
+
+    _native.lib()
+    if args.copy_probe:
+        copy_probe()
+        return
+    torch.cuda.set_device(0)
+    cids = [args.config] if args.config else list(DEFAULT_WORKLOADS)
+    results = []
+    for cid in cids:
+        results.append(run_workload(cid, args))
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    head = results[-1]
+    s = W.spec(cids[-1])
+    res = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "append": head["append"],
+        "workloads": [{k: r[k] for k in ("workload", "value", "unit", "ms_per_step", "roofline", "append")}
+                      for r in results],
+    }
     if not args.no_cpu_baseline:
         progress("timing the oracle on the host")
-        tps, threads, dt = cpu_baseline(s, min(args.cpu_seqs, s.batch), args.cpu_steps)
-        per_layer = f", one of {nlay} layers, rate divided by {nlay}" if nlay > 1 else ""
+        n_seq = min(args.cpu_seqs, s.batch)
+        tps, dt, lens = cpu_baseline(s, n_seq, args.cpu_steps)
+        cores, model = host_cpu()
+        per_layer = f", one of {s.layers} layers, rate divided by {s.layers}" if s.layers > 1 else ""
         res["cpu_baseline"] = {
-            "value": tps / nlay, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{min(args.cpu_seqs, s.batch)} of {s.batch} sequences x {args.cpu_steps} "
-                      f"decode steps (append + float64 attention){per_layer}, {dt:.1f} s"}
+            "value": tps / s.layers, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_seq} of {s.batch} sequences (lengths {lens}, the median ones) x "
+                      f"{args.cpu_steps} decode steps (append + float64 attention){per_layer}, "
+                      f"{dt:.1f} s, numpy BLAS held to 1 thread",
+            "host_cores": cores, "host_cpu": model}
     print(json.dumps(res), flush=True)
 
 

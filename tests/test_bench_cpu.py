@@ -97,17 +97,13 @@ class _Cache:
         self.len_host = list(other.len_host)
 
 
-@pytest.mark.parametrize("argv", [["--config", "1", "--steps", "5", "--warmup", "2", "--cpu-steps", "1"],
-                                  ["--config", "2", "--steps", "3", "--warmup", "2", "--no-cpu-baseline"]])
-def test_bench_main_with_gpu_calls_stubbed(argv, monkeypatch, capsys):
-    """bench.main() end to end on the CPU, every GPU call replaced by a stub:
-    the data flow (replicas, lengths, events, byte counts) and the JSON line."""
-    import json
+def _stub_gpu(monkeypatch):
     import torch
     import quantized_decode_attention_03_amd as K
 
     monkeypatch.setattr(torch.cuda, "Event", _Event)
     monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: None)
+    monkeypatch.setattr(torch.cuda, "empty_cache", lambda *a, **k: None)
     monkeypatch.setattr(torch.cuda, "set_device", lambda *a, **k: None)
     monkeypatch.setattr(torch.cuda, "current_stream", lambda *a, **k: None)
     monkeypatch.setattr(torch.Tensor, "to", lambda self, *a, **k: self)
@@ -122,6 +118,37 @@ def test_bench_main_with_gpu_calls_stubbed(argv, monkeypatch, capsys):
     monkeypatch.setattr(K, "KVCache", _Cache)
     monkeypatch.setattr(K, "kvq_append", append)
     monkeypatch.setattr(K, "kvq_decode_attention", lambda *a, **k: None)
+
+
+def test_bench_default_runs_three_workloads_headline_last(monkeypatch, capsys):
+    """With no --config, workloads 2, 4 and 5 run in turn (shrunk here so the
+    host generation stays small) and the headline fields are workload 5's."""
+    import json
+    _stub_gpu(monkeypatch)
+    small = {2: dict(batch=2, seq_len=300, min_len=300), 4: dict(batch=2, seq_len=400, min_len=400),
+             5: dict(batch=4, seq_len=600, min_len=100)}
+    specs = {cid: replace(W.SPECS[cid], **kw) for cid, kw in small.items()}
+    monkeypatch.setattr(W, "SPECS", {**W.SPECS, **specs})
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--steps", "3", "--warmup", "1", "--cpu-seqs", "2",
+                                      "--cpu-steps", "1", "--settle-ms", "0"])
+    bench.main()
+    d = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    assert [w["workload"] for w in d["workloads"]] == [specs[c].name for c in (2, 4, 5)]
+    assert d["config"]["workload"] == specs[5].name and d["value"] == d["workloads"][-1]["value"]
+    assert d["roofline"] == d["workloads"][-1]["roofline"]
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["host_cores"] >= 1 and cb["value"] > 0
+
+
+@pytest.mark.parametrize("argv", [["--config", "1", "--steps", "5", "--warmup", "2", "--cpu-steps", "1"],
+                                  ["--config", "2", "--steps", "3", "--warmup", "2", "--no-cpu-baseline"]])
+def test_bench_main_with_gpu_calls_stubbed(argv, monkeypatch, capsys):
+    """bench.main() end to end on the CPU, every GPU call replaced by a stub:
+    the data flow (replicas, lengths, events, byte counts) and the JSON line."""
+    import json
+    _stub_gpu(monkeypatch)
+    argv = argv + ["--settle-ms", "0"]
+
     monkeypatch.setattr(sys, "argv", ["bench.py"] + argv)
     bench.main()
     line = capsys.readouterr().out.strip().splitlines()[-1]
@@ -139,3 +166,4 @@ def test_bench_main_with_gpu_calls_stubbed(argv, monkeypatch, capsys):
     assert ("cpu_baseline" in d) == ("--no-cpu-baseline" not in argv)
     if "cpu_baseline" in d:
         assert d["cpu_baseline"]["kind"] == "oracle" and d["cpu_baseline"]["value"] > 0
+    assert len(d["workloads"]) == 1 and d["workloads"][0]["value"] == d["value"]
