@@ -185,8 +185,9 @@ kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch,
                            int64_t max_tokens, kvq_sizes* out_host);
 
 /* Bytes of device workspace kvq_decode_attention needs for this shape:
- * partial results (m, l, o[128] in fp32) of the work ranges that share a
- * (sequence, query head), at most max_tokens/256 + 2 of them. 0 on a bad
+ * partial results (m, l, o[128] in fp32 for each query head of a KV head),
+ * two per attention workgroup, for at most min(2048, batch * n_kv_heads *
+ * ceil(max_tokens / 32) / 8) workgroups (at most 17.3 MB). 0 on a bad
  * configuration or size (the rules of kvq_cache_sizes). Pure host function. */
 size_t kvq_workspace_bytes(const kvq_config* cfg, int32_t batch,
                            int64_t max_tokens);

@@ -92,9 +92,9 @@ void plan_attention(const kvq_config* cfg, const kvq_cache* cache, int64_t slots
   int64_t nwg = 0;
   if (U > 0) nwg = per > kMinUnitsPerWg ? std::max<int64_t>(1, U / per)
                                          : std::min<int64_t>(std::max<int64_t>(1, slots), std::max<int64_t>(1, U / per));
+  nwg = std::min<int64_t>(nwg, kMaxWgs);
   p->units = U;
   p->n_wg = (int)nwg;
-  p->max_parts = max_parts_for(cache->max_tokens);
   if (nwg > 1) {
     int64_t base = 0;
     for (int b = 0; b < cache->batch && !need; ++b) {
@@ -177,6 +177,35 @@ CacheView view_of(const kvq_config* cfg, const kvq_cache* c) {
   return v;
 }
 
+// Validation, plan and launch shared by the two attention entry points;
+// ws_bytes = 0 means ws is the library's own scratch (checked against the
+// plan instead of the shape bound).
+kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q, float* out,
+                            float softmax_scale, void* ws, size_t ws_bytes, bool own_scratch, void* stream) {
+  kvq_status s = check_config(cfg);
+  if (s != KVQ_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVQ_OK) return s;
+  if (!q || !out || !aligned(q) || !aligned(out)) return KVQ_EINVAL;
+  if (!own_scratch) {
+    if (!ws || !aligned(ws)) return KVQ_EINVAL;
+    if (ws_bytes < kvq_workspace_bytes(cfg, cache->batch, cache->max_tokens)) return KVQ_EWORKSPACE;
+  }
+  const CacheView v = view_of(cfg, cache);
+  // tile indices are 32-bit on the device
+  if ((int64_t)cache->batch * cfg->n_kv_heads * (cache->max_tokens / kBlock) > INT32_MAX) return KVQ_EUNSUPPORTED;
+  AttnPlan p;
+  p.Hq = cfg->n_q_heads;
+  p.group = cfg->n_q_heads / cfg->n_kv_heads;
+  p.scale = softmax_scale;
+  plan_attention(cfg, cache, (int64_t)compute_units() * attention_blocks_per_cu(v, p.group), &p);
+  if (own_scratch) {
+    if (workspace_bytes_for(p.n_wg, p.group) > ws_bytes) return KVQ_EWORKSPACE;
+    if (!ws) return KVQ_EHIP;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  return after_launch(launch_decode_attention(v, p, (const uint16_t*)q, out, (float*)ws, st), st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -220,7 +249,7 @@ kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch, int64_t max_tok
 
 size_t kvq_workspace_bytes(const kvq_config* cfg, int32_t batch, int64_t max_tokens) {
   if (check_config(cfg) != KVQ_OK || check_shape(batch, max_tokens) != KVQ_OK) return 0;
-  return (size_t)batch * cfg->n_q_heads * max_parts_for((int)max_tokens) * kPartialFloats * sizeof(float);
+  return workspace_bytes_for(max_wgs_for(batch, cfg->n_kv_heads, max_tokens), cfg->n_q_heads / cfg->n_kv_heads);
 }
 
 kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new, const void* v_new,
@@ -270,21 +299,7 @@ kvq_status kvq_append(const kvq_config* cfg, kvq_cache* cache, const void* k_new
 kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q,
                                 float* out, float softmax_scale, void* ws, size_t ws_bytes,
                                 void* stream) {
-  kvq_status s = check_config(cfg);
-  if (s != KVQ_OK) return s;
-  if ((s = check_cache(cfg, cache)) != KVQ_OK) return s;
-  if (!q || !out || !ws || !aligned(q) || !aligned(out) || !aligned(ws)) return KVQ_EINVAL;
-  if (ws_bytes < kvq_workspace_bytes(cfg, cache->batch, cache->max_tokens)) return KVQ_EWORKSPACE;
-  const CacheView v = view_of(cfg, cache);
-  // tile indices are 32-bit on the device
-  if ((int64_t)cache->batch * cfg->n_kv_heads * (cache->max_tokens / kBlock) > INT32_MAX) return KVQ_EUNSUPPORTED;
-  AttnPlan p;
-  p.Hq = cfg->n_q_heads;
-  p.group = cfg->n_q_heads / cfg->n_kv_heads;
-  p.scale = softmax_scale;
-  plan_attention(cfg, cache, (int64_t)compute_units() * attention_blocks_per_cu(v, p.group), &p);
-  hipStream_t st = (hipStream_t)stream;
-  return after_launch(launch_decode_attention(v, p, (const uint16_t*)q, out, (float*)ws, st), st);
+  return decode_attention(cfg, cache, q, out, softmax_scale, ws, ws_bytes, false, stream);
 }
 
 kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache, void* k_out, void* v_out,

@@ -525,6 +525,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   int u = (int)((int64_t)iwg * U / nwg);
   const UnitPos pos = locate_unit(c, u);
   int b = pos.b, base = pos.base;
+  bool first_seg = true;
   while (u < u1 && b < c.B) {
     // ---- the segment: tiles [k0, k1) of (sequence b, KV head h) -------------
     const int L = seq_len_of(c, b);
@@ -534,10 +535,11 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     const int h = rel / nt, k0 = rel - h * nt;
     const int k1 = min(nt, k0 + (u1 - u));
     // a segment that is the whole (sequence, KV head) writes the output;
-    // otherwise a partial result, numbered by the workgroup's position among
-    // those that share the (sequence, KV head)
+    // otherwise a partial result into the workgroup's slot for its first
+    // segment (2 iwg) or for its last one (2 iwg + 1): only those two can be
+    // pieces of a pair that other workgroups share
     const bool whole = k0 == 0 && k1 == nt;
-    const int part = iwg - wg_of_unit(base + h * nt, U, nwg);
+    const int slot = 2 * iwg + (first_seg ? 0 : 1);
     const size_t bh = (size_t)b * c.H + h;
     const int ts0 = min(k0 * kBlock, Q), ts1 = min(k1 * kBlock, Q);
     // This wavefront's quantized tiles: k = w, w + 4, ... over [ts0, ts1).
@@ -937,7 +939,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
       if (whole) {
         out[qh * kD + ch] = (l > 0.f) ? o / l : 0.f;
       } else {
-        float* pt = ws + (qh * p.max_parts + part) * kPartialFloats;
+        float* pt = ws + ((size_t)slot * G + hh) * kPartialFloats;
         if (ch == 0) { pt[0] = M; pt[1] = l; }
         pt[4 + ch] = o;
       }
@@ -945,6 +947,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     __syncthreads();  // the merge area is free again before the next segment's loads
 
     // ---- next segment -------------------------------------------------------
+    first_seg = false;
     u += k1 - k0;
     if (k1 == nt && h == c.H - 1) {
       base += c.H * nt;
@@ -965,7 +968,7 @@ __global__ __launch_bounds__(128) void combine_kernel(CacheView c, AttnPlan p, c
   constexpr int kBatch = 128;  // partials staged at a time
   __shared__ float pml[kBatch][2];
   const int bq = blockIdx.x, ch = threadIdx.x;
-  const int b = bq / p.Hq, hkv = (bq % p.Hq) / p.group;
+  const int b = bq / p.Hq, hkv = (bq % p.Hq) / p.group, hh = bq % p.group;
   const int L = seq_len_of(c, b);
   if (L == 0) {
     out[(size_t)bq * kD + ch] = 0.f;
@@ -973,16 +976,25 @@ __global__ __launch_bounds__(128) void combine_kernel(CacheView c, AttnPlan p, c
   }
   const int nt = units_of(c, L);
   const int s0 = units_before(c, b) + hkv * nt;  // the pair's units [s0, s0 + nt)
-  const int np = min(wg_of_unit(s0 + nt - 1, p.units, p.n_wg) - wg_of_unit(s0, p.units, p.n_wg) + 1, p.max_parts);
+  const int first = wg_of_unit(s0, p.units, p.n_wg), last = wg_of_unit(s0 + nt - 1, p.units, p.n_wg);
+  const int np = last - first + 1;
   if (np <= 1) return;  // written by the attention kernel
-  const float* part = ws + (size_t)bq * p.max_parts * kPartialFloats;
+  // the pair is the first segment of every workgroup of it but possibly the
+  // first one, where it is the last segment unless it starts the range
+  const bool mid_start = s0 != (int)((int64_t)first * p.units / p.n_wg);
+  auto rec = [&](int j) -> const float* {
+    const int wg = first + j;
+    const int slot = 2 * wg + ((j == 0 && mid_start) ? 1 : 0);
+    return ws + ((size_t)slot * p.group + hh) * kPartialFloats;
+  };
   float M = -INFINITY, o = 0.f, l = 0.f;
   for (int j0 = 0; j0 < np; j0 += kBatch) {
     const int n = min(kBatch, np - j0);
     __syncthreads();
     if (ch < n) {
-      pml[ch][0] = part[(j0 + ch) * kPartialFloats];
-      pml[ch][1] = part[(j0 + ch) * kPartialFloats + 1];
+      const float* pt = rec(j0 + ch);
+      pml[ch][0] = pt[0];
+      pml[ch][1] = pt[1];
     }
     __syncthreads();
     float mb = -INFINITY;
@@ -995,7 +1007,7 @@ __global__ __launch_bounds__(128) void combine_kernel(CacheView c, AttnPlan p, c
     for (int j = 0; j < n; j += 8) {
       float ov[8];
 #pragma unroll
-      for (int y = 0; y < 8; ++y) ov[y] = (j + y < n) ? part[(j0 + j + y) * kPartialFloats + 4 + ch] : 0.f;
+      for (int y = 0; y < 8; ++y) ov[y] = (j + y < n) ? rec(j0 + j + y)[4 + ch] : 0.f;
 #pragma unroll
       for (int y = 0; y < 8; ++y) {
         if (j + y < n) {

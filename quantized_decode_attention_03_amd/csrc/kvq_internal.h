@@ -52,7 +52,6 @@ struct AttnPlan {
   float scale;                 // softmax scale
   int64_t units;               // 32-token tiles of all (sequence, KV head) pairs
   int n_wg;                    // attention workgroups (each takes units / n_wg)
-  int max_parts;               // partial-result slots per (sequence, query head)
   int need_combine;            // some pair spans several workgroups, or a sequence is empty
 };
 hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p,
@@ -62,14 +61,23 @@ hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p,
 // compute unit (at least 1).
 int attention_blocks_per_cu(const CacheView& c, int group);
 
-// Workspace: fp32 partials [B][Hq][max_parts][kPartialFloats] = m, l, 2 pad,
-// o[128]. Every workgroup takes at least kMinUnitsPerWg tiles, so the tiles of
-// one (sequence, KV head), at most T/32, meet at most T/32/kMinUnitsPerWg + 2
-// workgroup ranges.
+// Workspace: fp32 partial results [2 n_wg][G][kPartialFloats] = m, l, 2 pad,
+// o[128]: two slots per attention workgroup (the first and the last segment
+// of its range, the only ones that can be pieces of a shared pair), each with
+// the G query heads of its KV head. Every workgroup takes at least
+// kMinUnitsPerWg tiles, and there are at most kMaxWgs of them.
 constexpr int kPartialFloats = 4 + kD;
 constexpr int kMinUnitsPerWg = 8;
-inline int max_parts_for(int max_tokens) {
-  return (max_tokens / kBlock + kMinUnitsPerWg - 1) / kMinUnitsPerWg + 2;
+constexpr int kMaxWgs = 2048;
+// Upper bound on the workgroups of an attention call for (batch, KV heads,
+// capacity): every (sequence, KV head) has at most ceil(T / 32) units.
+inline int64_t max_wgs_for(int64_t batch, int64_t n_kv_heads, int64_t max_tokens) {
+  const int64_t units = batch * n_kv_heads * ((max_tokens + kBlock - 1) / kBlock);
+  const int64_t by_units = units / kMinUnitsPerWg > 1 ? units / kMinUnitsPerWg : 1;
+  return by_units < kMaxWgs ? by_units : kMaxWgs;
+}
+inline size_t workspace_bytes_for(int64_t n_wg, int group) {
+  return (size_t)(2 * n_wg) * group * kPartialFloats * sizeof(float);
 }
 
 }  // namespace kvq

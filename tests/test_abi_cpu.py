@@ -131,6 +131,16 @@ def test_attention_errors_before_launch():
     assert L.kvq_dequantize(ctypes.byref(cfg), ctypes.byref(c), fake, fake, None) == N.KVQ_EINVAL
 
 
+def test_workspace_bound():
+    # two partial slots of G query heads per workgroup, at most 2048
+    # workgroups, each taking at least 8 tiles
+    slot = 132 * 4
+    assert kvq_workspace_bytes(_cfg(), 128, 32800) == 2 * 2048 * 4 * slot     # ragged int4 workload
+    assert kvq_workspace_bytes(_cfg(n_q_heads=64), 1, 4096) == 2 * (8 * 128 // 8) * 8 * slot
+    assert kvq_workspace_bytes(_cfg(n_kv_heads=1, n_q_heads=1), 1, 32) == 2 * 1 * 1 * slot
+    assert kvq_workspace_bytes(_cfg(n_q_heads=64), 128, 1 << 20) <= 17_301_504
+
+
 def test_status_strings():
     for s in range(6):
         assert N.status_string(s)
