@@ -226,6 +226,23 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 void* ws, size_t ws_bytes,
                                 void* stream /* hipStream_t */);
 
+/* kvq_decode_attention for callers that cannot allocate device memory or
+ * bring a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments and result, without ws: the
+ * partial results go to a scratch array the library holds in device memory,
+ * 17.3 MB on every GPU it runs on (looked up once per device with
+ * hipGetSymbolAddress), which bounds the work split to what
+ * kvq_workspace_bytes allows. It calls no allocating routine. Every call on
+ * one GPU shares that GPU's scratch, which keeps the last call's contents
+ * (nothing in it needs an initial value): calls that can overlap on one GPU
+ * (different streams, or threads without ordering) race; order them on one
+ * stream. Errors: as kvq_decode_attention; KVQ_EWORKSPACE if a call would need
+ * more scratch than held (not reachable within the checked shapes), KVQ_EHIP
+ * if the scratch address cannot be found. */
+kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const kvq_cache* cache,
+                                        const void* q, float* out, float softmax_scale,
+                                        void* stream /* hipStream_t */);
+
 /* Writes the dequantized cache as fp16 [B][T][H][D]: K_hat = fp16(s*(q - z))
  * plus sparse entries for quantized keys, the stored fp16 value for residual
  * keys, V_hat = fp16(s*(q - z)); token slots t >= seq_len[b] are written as

@@ -11,7 +11,7 @@ import ctypes
 from . import _native as N
 
 __all__ = ["Config", "KVCache", "kvq_cache_sizes", "kvq_workspace_bytes", "kvq_append",
-           "kvq_decode_attention", "kvq_dequantize", "KVQError"]
+           "kvq_decode_attention", "kvq_decode_attention_noalloc", "kvq_dequantize", "KVQError"]
 
 KVQError = N.KVQError
 
@@ -172,6 +172,19 @@ def kvq_decode_attention(cache, q, out, softmax_scale, ws, stream=None):
                                          _ptr(q), _ptr(out), ctypes.c_float(softmax_scale),
                                          _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()),
                                          _stream(stream)), "kvq_decode_attention")
+
+
+def kvq_decode_attention_noalloc(cache, q, out, softmax_scale, stream=None):
+    """kvq_decode_attention with the library's own device scratch instead of
+    a caller workspace (no allocation in the call). q: fp16 [B, Hq, D];
+    out: fp32 [B, Hq, D]."""
+    import torch
+    cfg, dev = cache.cfg, cache.device
+    _check(q, "q", torch.float16, (cache.batch, cfg.n_q_heads, cfg.d_head), dev)
+    _check(out, "out", torch.float32, (cache.batch, cfg.n_q_heads, cfg.d_head), dev)
+    N.check(N.lib().kvq_decode_attention_noalloc(ctypes.byref(cache._cfg), ctypes.byref(cache._c),
+                                                 _ptr(q), _ptr(out), ctypes.c_float(softmax_scale),
+                                                 _stream(stream)), "kvq_decode_attention_noalloc")
 
 
 def kvq_dequantize(cache, k_out, v_out, stream=None):

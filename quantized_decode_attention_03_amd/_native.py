@@ -15,7 +15,7 @@ KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EHIP = 
 KVQ_AXIS_TOKEN, KVQ_AXIS_CHANNEL = 0, 1
 
 EXPORTS = ("kvq_cache_sizes", "kvq_workspace_bytes", "kvq_append", "kvq_decode_attention",
-           "kvq_dequantize", "kvq_status_string")
+           "kvq_decode_attention_noalloc", "kvq_dequantize", "kvq_status_string")
 
 
 class kvq_config(ctypes.Structure):
@@ -67,6 +67,8 @@ def lib():
         L.kvq_decode_attention.argtypes = [cp(kvq_config), cp(kvq_cache), vp, vp, ctypes.c_float,
                                            vp, ctypes.c_size_t, vp]
         L.kvq_decode_attention.restype = ctypes.c_int
+        L.kvq_decode_attention_noalloc.argtypes = [cp(kvq_config), cp(kvq_cache), vp, vp, ctypes.c_float, vp]
+        L.kvq_decode_attention_noalloc.restype = ctypes.c_int
         L.kvq_dequantize.argtypes = [cp(kvq_config), cp(kvq_cache), vp, vp, vp]
         L.kvq_dequantize.restype = ctypes.c_int
         L.kvq_status_string.argtypes = [ctypes.c_int]

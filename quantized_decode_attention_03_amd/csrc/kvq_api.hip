@@ -206,6 +206,32 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, const
   return after_launch(launch_decode_attention(v, p, (const uint16_t*)q, out, (float*)ws, st), st);
 }
 
+// Scratch of the entry point that allocates nothing: the largest workspace an
+// attention call can need (kMaxWgs workgroups, two partial slots each, 8 query
+// heads per KV head), 17.3 MB, held on every device the library runs on until
+// the process ends. Host code uses the device address from
+// hipGetSymbolAddress, never the array's name (a host-side stand-in).
+constexpr size_t kScratchBytes = (size_t)2 * kMaxWgs * 8 * kPartialFloats * sizeof(float);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (threads may race to store the same value); nullptr if the lookup fails.
+void* scratch_address() {
+  static std::atomic<void*> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = cache[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      if (debug_sync()) fprintf(stderr, "kvq: hipGetSymbolAddress of the attention scratch failed\n");
+      return nullptr;
+    }
+    cache[dev].store(p, std::memory_order_relaxed);
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -300,6 +326,16 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
                                 float* out, float softmax_scale, void* ws, size_t ws_bytes,
                                 void* stream) {
   return decode_attention(cfg, cache, q, out, softmax_scale, ws, ws_bytes, false, stream);
+}
+
+kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                                        float* out, float softmax_scale, void* stream) {
+  // validate before touching the device, so argument errors need no HIP call
+  kvq_status s = check_config(cfg);
+  if (s != KVQ_OK) return s;
+  if ((s = check_cache(cfg, cache)) != KVQ_OK) return s;
+  if (!q || !out || !aligned(q) || !aligned(out)) return KVQ_EINVAL;
+  return decode_attention(cfg, cache, q, out, softmax_scale, scratch_address(), kScratchBytes, true, stream);
 }
 
 kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache, void* k_out, void* v_out,

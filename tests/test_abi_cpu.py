@@ -129,6 +129,15 @@ def test_attention_errors_before_launch():
     assert L.kvq_decode_attention(ctypes.byref(cfg), ctypes.byref(c), fake, fake, ctypes.c_float(0.1),
                                   fake, need, None) == N.KVQ_EINVAL
     assert L.kvq_dequantize(ctypes.byref(cfg), ctypes.byref(c), fake, fake, None) == N.KVQ_EINVAL
+    # the entry point without a workspace validates the same way, before any HIP call
+    assert L.kvq_decode_attention_noalloc(ctypes.byref(cfg), ctypes.byref(c), fake, fake,
+                                          ctypes.c_float(0.1), None) == N.KVQ_EINVAL
+    c.len_host[0] = 10
+    assert L.kvq_decode_attention_noalloc(ctypes.byref(cfg), ctypes.byref(c), None, fake,
+                                          ctypes.c_float(0.1), None) == N.KVQ_EINVAL
+    mis = ctypes.c_void_p((1 << 20) + 4)
+    assert L.kvq_decode_attention_noalloc(ctypes.byref(cfg), ctypes.byref(c), fake, mis,
+                                          ctypes.c_float(0.1), None) == N.KVQ_EINVAL
 
 
 def test_workspace_bound():
@@ -138,7 +147,7 @@ def test_workspace_bound():
     assert kvq_workspace_bytes(_cfg(), 128, 32800) == 2 * 2048 * 4 * slot     # ragged int4 workload
     assert kvq_workspace_bytes(_cfg(n_q_heads=64), 1, 4096) == 2 * (8 * 128 // 8) * 8 * slot
     assert kvq_workspace_bytes(_cfg(n_kv_heads=1, n_q_heads=1), 1, 32) == 2 * 1 * 1 * slot
-    assert kvq_workspace_bytes(_cfg(n_q_heads=64), 128, 1 << 20) <= 17_301_504
+    assert kvq_workspace_bytes(_cfg(n_q_heads=64), 128, 1 << 20) <= 17_301_504  # the scratch held for the no-allocation call
 
 
 def test_status_strings():
