@@ -25,6 +25,28 @@
  *   - Decode attention that streams the packed cache and dequantizes on the
  *     fly ("KV Cache Quantization — 8-bit and 4-bit", "Decode is memory-bound,
  *     so smaller is also faster").
+ *   - Two more element formats for token-axis caches ("KV Cache Quantization
+ *     Benchmarked: 8-bit Is Nearly Lossless, How Much Does 4-bit Cost?", the
+ *     glossary and memory paragraphs: an fp8 cache with a 4-bit exponent and
+ *     a 3-bit mantissa, and llama.cpp-style blocks of 32 elements sharing one
+ *     scale; "KV Cache Quantization — 8-bit and 4-bit", "Symmetric vs
+ *     asymmetric" for the zero point forced to zero):
+ *       KVQ_FORMAT_FP8:   one OCP E4M3 byte per element (sign bit 7, exponent
+ *                         bits 6..3 with bias 7, mantissa bits 2..0; no
+ *                         infinities, S.1111.111 is NaN, largest finite 448)
+ *                         and one fp32 scale per cache side:
+ *                         code = e4m3(x / scale), x_hat = scale * value(code).
+ *                         e4m3() rounds to the nearest magnitude, ties to the
+ *                         even code, saturates above 448 and keeps the sign
+ *                         (a negative value that rounds to zero is 0x80).
+ *       KVQ_FORMAT_SYM32: each token vector cut into 4 blocks of 32
+ *                         consecutive channels; per block
+ *                         s16 = smallest fp16 >= max|x| / (float)q_max
+ *                         (1.0 for an all-zero block), s = (float)s16,
+ *                         q_i = clamp(rint(x_i / s), -q_max, q_max),
+ *                         stored u_i = q_i - q_min, x_hat_i = s * q_i.
+ *     Both formats keep keys on the token axis and apply to keys and values
+ *     alike (k_format == v_format).
  *
  * Exact arithmetic of one quantization group (x_i are fp16 values widened to
  * fp32; every operation is IEEE fp32 with round-to-nearest-even):
@@ -84,6 +106,10 @@
  *            of byte (tau*vb)/8 of the record.
  *   v_meta   uint32 meta word [B][H][T]
  *   seq_len  int32 [B]
+ * KVQ_FORMAT_FP8 caches have no k_meta or v_meta (size 0; the pointers may be
+ * NULL); their codes are the E4M3 bytes, in the 8-bit layouts above.
+ * KVQ_FORMAT_SYM32 caches store k_meta and v_meta as fp16 [B][H][T][4] (the
+ * scales of channel blocks 0..31, 32..63, 64..95, 96..127 of each token).
  * Code bits of token slots >= L inside a byte written by the library are 0.
  * Buffers must be zero-filled before the first append of a sequence.
  *
@@ -136,6 +162,7 @@ typedef enum kvq_status {
 } kvq_status;
 
 enum { KVQ_AXIS_TOKEN = 0, KVQ_AXIS_CHANNEL = 1 };
+enum { KVQ_FORMAT_INT = 0, KVQ_FORMAT_FP8 = 1, KVQ_FORMAT_SYM32 = 2 };
 
 /* Quantization configuration, passed by value through a host pointer. */
 typedef struct kvq_config {
@@ -150,6 +177,10 @@ typedef struct kvq_config {
                                   axis, 0 for token axis                     */
   int32_t v_group_channels;    /* channels per value group; must be d_head   */
   int32_t k_sparse_per_vector; /* 0, or 2 (channel axis only)                */
+  int32_t k_format;            /* KVQ_FORMAT_*; 0 (INT) for the affine codes */
+  int32_t v_format;            /* equal to k_format                          */
+  float k_scale;               /* FP8 only: per-cache key scale, finite > 0  */
+  float v_scale;               /* FP8 only: per-cache value scale            */
 } kvq_config;
 
 /* Host-side descriptor of one cache; pointers name device memory except

@@ -16,11 +16,17 @@ __all__ = ["Config", "KVCache", "kvq_cache_sizes", "kvq_workspace_bytes", "kvq_a
 KVQError = N.KVQError
 
 
+_FORMATS = {"int": N.KVQ_FORMAT_INT, "fp8": N.KVQ_FORMAT_FP8, "sym32": N.KVQ_FORMAT_SYM32}
+
+
 class Config:
-    """Mirror of kvq_config. k_axis is "token" or "channel"."""
+    """Mirror of kvq_config. k_axis is "token" or "channel"; k_format and
+    v_format are "int" (affine codes), "fp8" (E4M3 with the per-cache scales
+    k_scale, v_scale) or "sym32" (symmetric 32-channel blocks)."""
 
     def __init__(self, n_kv_heads, n_q_heads, k_bits, v_bits, k_axis="token",
-                 k_group_tokens=0, k_residual_tokens=0, k_sparse_per_vector=0, d_head=128):
+                 k_group_tokens=0, k_residual_tokens=0, k_sparse_per_vector=0, d_head=128,
+                 k_format="int", v_format=None, k_scale=1.0, v_scale=1.0):
         self.d_head = d_head
         self.n_kv_heads = n_kv_heads
         self.n_q_heads = n_q_heads
@@ -30,18 +36,26 @@ class Config:
         self.k_group_tokens = k_group_tokens
         self.k_residual_tokens = k_residual_tokens
         self.k_sparse_per_vector = k_sparse_per_vector
+        self.k_format = k_format
+        self.v_format = k_format if v_format is None else v_format
+        for f in (self.k_format, self.v_format):
+            if f not in _FORMATS:
+                raise ValueError(f"format {f!r}: expected one of {sorted(_FORMATS)}")
+        self.k_scale = k_scale
+        self.v_scale = v_scale
 
     @classmethod
     def from_spec(cls, s):
         return cls(s.n_kv_heads, s.n_q_heads, s.k_bits, s.v_bits, s.k_axis, s.k_group,
-                   s.k_residual, s.k_sparse, s.d_head)
+                   s.k_residual, s.k_sparse, s.d_head, s.fmt, s.fmt, s.k_scale, s.v_scale)
 
     def c(self):
         return N.kvq_config(self.d_head, self.n_kv_heads, self.n_q_heads, self.k_bits,
                             self.v_bits,
                             N.KVQ_AXIS_CHANNEL if self.k_axis == "channel" else N.KVQ_AXIS_TOKEN,
                             self.k_group_tokens, self.k_residual_tokens, self.d_head,
-                            self.k_sparse_per_vector)
+                            self.k_sparse_per_vector, _FORMATS[self.k_format],
+                            _FORMATS[self.v_format], self.k_scale, self.v_scale)
 
 
 def _ptr(t):

@@ -13,6 +13,7 @@ LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(HERE, "libkvq.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EHIP = range(6)
 KVQ_AXIS_TOKEN, KVQ_AXIS_CHANNEL = 0, 1
+KVQ_FORMAT_INT, KVQ_FORMAT_FP8, KVQ_FORMAT_SYM32 = 0, 1, 2
 
 EXPORTS = ("kvq_cache_sizes", "kvq_workspace_bytes", "kvq_append", "kvq_decode_attention",
            "kvq_decode_attention_noalloc", "kvq_dequantize", "kvq_status_string")
@@ -21,7 +22,8 @@ EXPORTS = ("kvq_cache_sizes", "kvq_workspace_bytes", "kvq_append", "kvq_decode_a
 class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_head", "n_kv_heads", "n_q_heads", "k_bits", "v_bits", "k_axis", "k_group_tokens",
-        "k_residual_tokens", "v_group_channels", "k_sparse_per_vector")]
+        "k_residual_tokens", "v_group_channels", "k_sparse_per_vector", "k_format",
+        "v_format")] + [("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class kvq_cache(ctypes.Structure):

@@ -121,6 +121,15 @@ kvq_status check_config(const kvq_config* cfg) {
   if (cfg->d_head != kD) return KVQ_EUNSUPPORTED;
   if (cfg->v_group_channels != cfg->d_head) return KVQ_EUNSUPPORTED;
   if (!bits_ok(cfg->k_bits) || !bits_ok(cfg->v_bits)) return KVQ_EUNSUPPORTED;
+  const int fmt = cfg->k_format;
+  if (fmt != KVQ_FORMAT_INT && fmt != KVQ_FORMAT_FP8 && fmt != KVQ_FORMAT_SYM32) return KVQ_EINVAL;
+  if (cfg->v_format != fmt) return KVQ_EUNSUPPORTED;  // one format for keys and values
+  if (fmt != KVQ_FORMAT_INT && cfg->k_axis != KVQ_AXIS_TOKEN) return KVQ_EUNSUPPORTED;
+  if (fmt == KVQ_FORMAT_FP8) {
+    if (cfg->k_bits != 8 || cfg->v_bits != 8) return KVQ_EINVAL;
+    for (float sc : {cfg->k_scale, cfg->v_scale})
+      if (!(sc > 0.0f) || !std::isfinite(sc)) return KVQ_EINVAL;
+  }
   if (cfg->k_axis == KVQ_AXIS_TOKEN) {
     if (cfg->k_group_tokens != 0 || cfg->k_residual_tokens != 0) return KVQ_EINVAL;
     if (cfg->k_sparse_per_vector != 0) return KVQ_EUNSUPPORTED;
@@ -146,9 +155,13 @@ kvq_status check_cache(const kvq_config* cfg, const kvq_cache* c) {
   if (!c) return KVQ_EINVAL;
   kvq_status s = check_shape(c->batch, c->max_tokens);
   if (s != KVQ_OK) return s;
-  const void* req[] = {c->k_codes, c->k_meta, c->v_codes, c->v_meta, c->seq_len};
+  const void* req[] = {c->k_codes, c->v_codes, c->seq_len};
   for (const void* p : req)
     if (!p || !aligned(p)) return KVQ_EINVAL;
+  if (cfg->k_format != KVQ_FORMAT_FP8) {  // fp8 caches have no metadata arrays
+    for (const void* p : {c->k_meta, c->v_meta})
+      if (!p || !aligned(p)) return KVQ_EINVAL;
+  }
   if (!c->len_host) return KVQ_EINVAL;
   if (cfg->k_axis == KVQ_AXIS_CHANNEL && (!c->k_resid || !aligned(c->k_resid))) return KVQ_EINVAL;
   if (cfg->k_sparse_per_vector && (!c->k_sparse || !aligned(c->k_sparse))) return KVQ_EINVAL;
@@ -167,6 +180,9 @@ CacheView view_of(const kvq_config* cfg, const kvq_cache* c) {
   v.kaxis = cfg->k_axis == KVQ_AXIS_CHANNEL ? 1 : 0;
   v.R = cfg->k_residual_tokens;
   v.sparse = cfg->k_sparse_per_vector;
+  v.fmt = cfg->k_format == KVQ_FORMAT_FP8 ? kFmtFp8 : (cfg->k_format == KVQ_FORMAT_SYM32 ? kFmtSym32 : kFmtInt);
+  v.kscale = cfg->k_scale;
+  v.vscale = cfg->v_scale;
   v.k_codes = (uint8_t*)c->k_codes;
   v.k_meta = (uint32_t*)c->k_meta;
   v.k_resid = (uint16_t*)c->k_resid;
@@ -258,14 +274,16 @@ kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch, int64_t max_tok
   memset(out, 0, sizeof(*out));
   out->k_codes = n * T * D * cfg->k_bits / 8;
   out->v_codes = n * T * D * cfg->v_bits / 8;
-  out->v_meta = n * T * 4;
+  // metadata per token: one word (affine), 4 fp16 block scales (sym32), none (fp8)
+  const uint64_t meta_tok = cfg->k_format == KVQ_FORMAT_FP8 ? 0 : (cfg->k_format == KVQ_FORMAT_SYM32 ? 2 * kSymBlocks : 4);
+  out->v_meta = n * T * meta_tok;
   out->seq_len = (uint64_t)batch * 4;
   if (cfg->k_axis == KVQ_AXIS_CHANNEL) {
     out->k_meta = n * (T / kBlock) * D * 4;
     out->k_resid = n * (uint64_t)cfg->k_residual_tokens * D * 2;
     out->k_sparse = cfg->k_sparse_per_vector ? n * T * 8 : 0;
   } else {
-    out->k_meta = n * T * 4;
+    out->k_meta = n * T * meta_tok;
   }
   out->nominal_bytes = n * T * D * (cfg->k_bits + cfg->v_bits) / 8;
   out->total_bytes = out->k_codes + out->k_meta + out->k_resid + out->k_sparse + out->v_codes +

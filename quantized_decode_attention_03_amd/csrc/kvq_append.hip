@@ -2,7 +2,9 @@
 //
 // Values, and keys on the token axis, are quantized one token vector (128
 // channels) at a time: one wavefront per token, two channels per lane, a
-// cross-lane min/max reduction along the channel axis. Keys on the channel
+// cross-lane min/max reduction along the channel axis (max |x| over 16 lanes
+// per 32-channel block for symmetric blocks; none for fp8, whose scale is per
+// cache). Keys on the channel
 // axis wait in the fp16 residual window; a window that fills is quantized as
 // groups of one channel over 32 consecutive tokens (a min/max along the token
 // axis), after the dense-and-sparse split when it is enabled. (KIVI's axis
@@ -38,6 +40,31 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
     v = v > o ? v : o;
   }
   return v;
+}
+
+// Stored codes of channels 2 lane and 2 lane + 1 (values f0, f1) of one token
+// vector held by a wavefront, in the cache's element format; the token's
+// metadata goes to the token's slot `tok` of `meta`:
+//   affine codes: one meta word per token (group = the 128 channels);
+//   symmetric blocks: 4 fp16 scales per token (group = 32 channels = 16 lanes);
+//   fp8: no metadata; code = e4m3(x / scale).
+__device__ __forceinline__ uint2 quant_token(float f0, float f1, int fmt, int bits, float scale,
+                                             uint32_t* meta, size_t tok, int lane) {
+#pragma clang fp contract(off)
+  if (fmt == kFmtFp8) return make_uint2(e4m3_code(f0 / scale), e4m3_code(f1 / scale));
+  if (fmt == kFmtSym32) {
+    float a = __builtin_fmaxf(__builtin_fabsf(f0), __builtin_fabsf(f1));
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off, 64));
+    const uint16_t s16 = sym_scale16(a, bits);
+    if ((lane & 15) == 0) reinterpret_cast<uint16_t*>(meta)[tok * kSymBlocks + (lane >> 4)] = s16;
+    const float sc = h2f(s16);
+    return make_uint2(sym_code(f0, sc, bits), sym_code(f1, sc, bits));
+  }
+  const float mn = wave_min(__builtin_fminf(f0, f1)), mx = wave_max(__builtin_fmaxf(f0, f1));
+  const GroupQ g = group_params(mn, mx, bits);
+  if (lane == 0) meta[tok] = g.meta;
+  return make_uint2(quant_code(f0, g, bits), quant_code(f1, g, bits));
 }
 
 // Sequence b's state before the append: L tokens held, its new tokens are
@@ -172,21 +199,17 @@ __global__ __launch_bounds__(256) void append_tokens_kernel(CacheView c, AppendI
     const size_t src = ((size_t)(row0 + t - L) * c.H + h) * kD;
     {
       const uint32_t pr = reinterpret_cast<const uint32_t*>(in.v_new + src)[lane];
-      const float f0 = h2f((uint16_t)(pr & 0xFFFFu)), f1 = h2f((uint16_t)(pr >> 16));
-      const float mn = wave_min(__builtin_fminf(f0, f1)), mx = wave_max(__builtin_fmaxf(f0, f1));
-      const GroupQ g = group_params(mn, mx, c.vbits);
-      vcodes[tau][2 * lane] = (uint8_t)quant_code(f0, g, c.vbits);
-      vcodes[tau][2 * lane + 1] = (uint8_t)quant_code(f1, g, c.vbits);
-      if (lane == 0) c.v_meta[bh * c.T + t] = g.meta;
+      const uint2 u = quant_token(h2f((uint16_t)(pr & 0xFFFFu)), h2f((uint16_t)(pr >> 16)), c.fmt, c.vbits,
+                                  c.vscale, c.v_meta, bh * c.T + t, lane);
+      vcodes[tau][2 * lane] = (uint8_t)u.x;
+      vcodes[tau][2 * lane + 1] = (uint8_t)u.y;
     }
     const uint32_t pk = reinterpret_cast<const uint32_t*>(in.k_new + src)[lane];
     if (ktok) {
-      const float f0 = h2f((uint16_t)(pk & 0xFFFFu)), f1 = h2f((uint16_t)(pk >> 16));
-      const float mn = wave_min(__builtin_fminf(f0, f1)), mx = wave_max(__builtin_fmaxf(f0, f1));
-      const GroupQ g = group_params(mn, mx, c.kbits);
-      kcodes[tau][2 * lane] = (uint8_t)quant_code(f0, g, c.kbits);
-      kcodes[tau][2 * lane + 1] = (uint8_t)quant_code(f1, g, c.kbits);
-      if (lane == 0) c.k_meta[bh * c.T + t] = g.meta;
+      const uint2 u = quant_token(h2f((uint16_t)(pk & 0xFFFFu)), h2f((uint16_t)(pk >> 16)), c.fmt, c.kbits,
+                                  c.kscale, c.k_meta, bh * c.T + t, lane);
+      kcodes[tau][2 * lane] = (uint8_t)u.x;
+      kcodes[tau][2 * lane + 1] = (uint8_t)u.y;
     } else if (t >= Q2) {
       reinterpret_cast<uint32_t*>(c.k_resid + (bh * c.R + (t - Q2)) * kD)[lane] = pk;
     }
@@ -244,11 +267,9 @@ __global__ __launch_bounds__(256) void append_decode_kernel(CacheView c, AppendI
     const uint32_t pr = reinterpret_cast<const uint32_t*>(in.v_new + src)[lane];
     const uint32_t pk = reinterpret_cast<const uint32_t*>(in.k_new + src)[lane];
     {  // value codes of channels 2 lane and 2 lane + 1 into their records
-      const float f0 = h2f((uint16_t)(pr & 0xFFFFu)), f1 = h2f((uint16_t)(pr >> 16));
-      const float mn = wave_min(__builtin_fminf(f0, f1)), mx = wave_max(__builtin_fmaxf(f0, f1));
-      const GroupQ g = group_params(mn, mx, c.vbits);
-      const uint32_t u0 = quant_code(f0, g, c.vbits), u1 = quant_code(f1, g, c.vbits);
-      if (lane == 0) c.v_meta[bh * c.T + t] = g.meta;
+      const uint2 u = quant_token(h2f((uint16_t)(pr & 0xFFFFu)), h2f((uint16_t)(pr >> 16)), c.fmt, c.vbits,
+                                  c.vscale, c.v_meta, bh * c.T + t, lane);
+      const uint32_t u0 = u.x, u1 = u.y;
       const int vb = c.vbits, per = 32 / vb, wd = tau / per, f = tau % per;
       // fields of earlier tokens in the word are kept, later ones are zero
       const uint32_t keep = (1u << (f * vb)) - 1u;
@@ -260,11 +281,9 @@ __global__ __launch_bounds__(256) void append_decode_kernel(CacheView c, AppendI
       *p1 = (o1 & keep) | (u1 << (f * vb));
     }
     if (ktok) {  // the token's key row, channels packed low bits first
-      const float f0 = h2f((uint16_t)(pk & 0xFFFFu)), f1 = h2f((uint16_t)(pk >> 16));
-      const float mn = wave_min(__builtin_fminf(f0, f1)), mx = wave_max(__builtin_fmaxf(f0, f1));
-      const GroupQ g = group_params(mn, mx, c.kbits);
-      const uint32_t u0 = quant_code(f0, g, c.kbits), u1 = quant_code(f1, g, c.kbits);
-      if (lane == 0) c.k_meta[bh * c.T + t] = g.meta;
+      const uint2 u = quant_token(h2f((uint16_t)(pk & 0xFFFFu)), h2f((uint16_t)(pk >> 16)), c.fmt, c.kbits,
+                                  c.kscale, c.k_meta, bh * c.T + t, lane);
+      const uint32_t u0 = u.x, u1 = u.y;
       uint8_t* row = c.k_codes + (bh * c.T + t) * (size_t)(16 * c.kbits);
       if (c.kbits == 8) {
         reinterpret_cast<uint16_t*>(row)[lane] = (uint16_t)(u0 | (u1 << 8));

@@ -40,6 +40,16 @@
 //   values, token axis: x = s_t (u - z'_t); P = p_t * s_t * 2^kv as hi/lo rows
 //     h and g + h; the product with a B operand whose columns all hold z'_t
 //     is subtracted once at the end.
+// The two other element formats keep keys on the token axis:
+//   fp8 E4M3: bytes become fp16 operands exactly (a hardware conversion; every
+//     E4M3 value is an fp16 value); the per-cache key scale multiplies the
+//     score, the value scale the output; no zero points, and P = p;
+//   symmetric 32-channel blocks: x = s_t,j (u + q_min) for block j of token
+//     t. Keys: each block gets its own MFMA (the lane groups' k-slots all in
+//     block j), seeded with q_min * (sum of the block's query channels), and
+//     the token's block scales combine the four products; values: one P
+//     operand per block (p_t * s_t,j * 2^kv) for its two 16-channel chunks, and
+//     the constant zero point -q_min through one more MFMA per block.
 // The hi and lo parts of the scaled query sit in different columns of one B
 // operand (column n: head n mod g, hi part when n / g is even), so one MFMA
 // covers both; one DPP add across lanes n and n - g of a 16-lane row sums
@@ -252,24 +262,61 @@ __device__ __forceinline__ void val_words(const uint8_t* rec, int grp, uint32_t&
   }
 }
 
+// fp8 E4M3 bytes to an fp16 operand: bytes (0, 1) and (2, 3) of a, then of b,
+// as k-slot pairs 0..3 (the 8-bit layout of key_frag and val_frag). Every
+// E4M3 value is an fp16 value, so the conversion (scale 1) is exact.
+__device__ __forceinline__ Frag fp8_frag(uint32_t a, uint32_t b) {
+  Frag f;
+  f.p[0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, false));
+  f.p[1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, true));
+  f.p[2] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false));
+  f.p[3] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, true));
+  return f;
+}
+
+// Key operand of one 32-channel block for symmetric block codes: MFMA j takes
+// block j, and lane group g its k-slots, the channels key_channel(j, g, ...)
+// (the roles of the lane group and the chunk swapped against the affine
+// layout). The lane's words (row bytes [32 j + 8 g, +8) for 8-bit codes,
+// [16 j + 4 g, +4) for 4-bit, [8 j + 4 (g / 2), +4) shifted right by 8 (g mod
+// 2) for 2-bit) hold exactly those channels.
+template <int KB>
+__device__ __forceinline__ Frag sym_key_frag(uint32_t w0, uint32_t w1) {
+  Frag f;
+  if constexpr (KB == 8) {
+    f.p[0] = perm(0u, w0, 0x0C010C00u);
+    f.p[1] = perm(0u, w0, 0x0C030C02u);
+    f.p[2] = perm(0u, w1, 0x0C010C00u);
+    f.p[3] = perm(0u, w1, 0x0C030C02u);
+  } else {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) f.p[p] = field_pair<KB>(w0, KB * p);
+  }
+  return f;
+}
+
 // Geometry of one 32-token tile as staged in LDS:
-//   [key codes 32 x 16*KB][value block 128 x 4*VB][value meta 32 words]
-//   [key meta: 128 words (channel axis) or 32 (token axis)][sparse 32 x 2 words]
-// Key codes and the value block are contiguous in global memory and move
-// with 1 KiB direct-to-LDS loads (64 lanes x 16 bytes); the metadata pieces
-// follow with one load per array, each lane group gathering 16-byte chunks
-// into consecutive LDS.
-template <int KB, int VB, int KAXIS, int G, bool SPARSE>
+//   [key codes 32 x 16*KB][value block 128 x 4*VB][value meta, 32 tokens]
+//   [key meta: 128 words (channel axis) or 32 tokens (token axis)]
+//   [sparse 32 x 2 words]
+// Metadata per token: one word (affine codes), 4 fp16 block scales (symmetric
+// blocks), none (fp8). Key codes and the value block are contiguous in global
+// memory and move with 1 KiB direct-to-LDS loads (64 lanes x 16 bytes); the
+// metadata pieces follow with one load per array, each lane group gathering
+// 16-byte chunks into consecutive LDS.
+template <int KB, int VB, int KAXIS, int G, bool SPARSE, int FMT>
 struct Geom {
   static constexpr int kRowK = 16 * KB;               // key code bytes per token
   static constexpr int kK = 32 * kRowK;               // key codes of a tile
   static constexpr int kV = 512 * VB;                 // value block
-  static constexpr int kVm = 128;
-  static constexpr int kKm = KAXIS ? 512 : 128;
+  static constexpr int kMetaTok = FMT == kFmtFp8 ? 0 : (FMT == kFmtSym32 ? 2 * kSymBlocks : 4);
+  static constexpr int kVm = 32 * kMetaTok;
+  static constexpr int kKm = KAXIS ? 512 : 32 * kMetaTok;
   static constexpr int kSp = SPARSE ? 256 : 0;
   static constexpr int kMetaLanes = (kVm + kKm + kSp) / 16;
+  static constexpr int kMetaLoads = (kVm > 0) + (kKm > 0) + (SPARSE ? 1 : 0);
   static constexpr int kBytes = kK + kV + kVm + kKm + kSp;
-  static constexpr int kLoads = kK / 1024 + kV / 1024 + (SPARSE ? 3 : 2);  // DMA instructions per tile
+  static constexpr int kLoads = kK / 1024 + kV / 1024 + kMetaLoads;  // DMA instructions per tile
   // the key-product B operand and zero-point operand (channel axis only)
   static constexpr int kWaveLds = KAXIS ? (4 * (2 * G) * 4 * 16 + 4 * 4 * 4 * 4) : 0;
   // tile slots per wavefront: as many as fit the per-wavefront budget, 2 to 6
@@ -461,10 +508,13 @@ __device__ int units_before(const CacheView& c, int b) {
   return __builtin_amdgcn_readfirstlane(sum);
 }
 
-template <int KB, int VB, int KAXIS, int G, bool SPARSE>
+template <int KB, int VB, int KAXIS, int G, bool SPARSE, int FMT>
 __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, const uint16_t* __restrict__ q,
                                                    float* __restrict__ out, float* __restrict__ ws) {
-  using Gm = Geom<KB, VB, KAXIS, G, SPARSE>;
+  using Gm = Geom<KB, VB, KAXIS, G, SPARSE, FMT>;
+  constexpr bool kFp8 = FMT == kFmtFp8, kSym = FMT == kFmtSym32;
+  static_assert(FMT == kFmtInt || (KAXIS == 0 && !SPARSE), "fp8 and block formats are token-axis only");
+  static_assert(!kFp8 || (KB == 8 && VB == 8), "fp8 codes are bytes");
   constexpr int NB = Gm::kSlots;
   constexpr int kQMinK = -(1 << (KB - 1));
   constexpr int kQMinV = -(1 << (VB - 1));
@@ -479,6 +529,14 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   constexpr int kKvTop = 20;
   constexpr _Float16 kZv = (_Float16)pow2f(kShV - 24);                // value code step
   constexpr _Float16 kZvOfs = (_Float16)(-kQMinV * pow2f(kShV - 24));  // -q_min in code steps
+  // symmetric blocks: x = s (u + q_min), so the zero point in code steps is
+  // -q_min for every token: a constant B operand
+  const Frag bsym = {{(uint32_t)(-kQMinV << kShV) * 0x10001u, (uint32_t)(-kQMinV << kShV) * 0x10001u,
+                      (uint32_t)(-kQMinV << kShV) * 0x10001u, (uint32_t)(-kQMinV << kShV) * 0x10001u}};
+  // value blocks feeding one P.V product (one per 32-channel block for
+  // symmetric blocks, whose scales differ per block)
+  constexpr int kPB = kSym ? kSymBlocks : 1;
+  constexpr int kVmW = kSym ? 16 : 8;  // value meta words of the lane's 8 tokens
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -515,8 +573,8 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   const h2v zofs = h2_splat((uint16_t)(0x8000u | (1u << (bsh + KB - 1))));
   // residual keys are plain fp16: their "scale" 2^(bsh - kShK) cancels the factor
   const uint32_t kres = (uint32_t)(15 + bsh - kShK) << 10;
-  // metadata lanes of the tile loads: 0..7 value scales, then key scales, then sparse entries
-  const int mkind = lane < 8 ? 0 : (lane < 8 + Gm::kKm / 16 ? 1 : 2);
+  // metadata lanes of the tile loads: value scales, then key scales, then sparse entries
+  const int mkind = lane < Gm::kVm / 16 ? 0 : (lane < (Gm::kVm + Gm::kKm) / 16 ? 1 : 2);
 
   // this workgroup's units
   const int nwg = gridDim.x, iwg = blockIdx.x;
@@ -559,22 +617,23 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     const uint32_t Tu = (uint32_t)c.T;
     const u32x4 rk = make_rsrc(c.k_codes + bh * c.T * (size_t)Gm::kRowK, Tu * Gm::kRowK);
     const u32x4 rv = make_rsrc(c.v_codes + bh * (c.T / kBlock) * (size_t)Gm::kV, (Tu / kBlock) * Gm::kV);
-    const u32x4 rvm = make_rsrc(c.v_meta + bh * c.T, Tu * 4);
+    constexpr int kMt = Gm::kMetaTok;
+    const u32x4 rvm = make_rsrc(reinterpret_cast<const uint8_t*>(c.v_meta) + bh * c.T * kMt, Tu * kMt);
     const u32x4 rkm = KAXIS ? make_rsrc(c.k_meta + bh * (c.T / kBlock) * kD, (Tu / kBlock) * kD * 4)
-                            : make_rsrc(c.k_meta + bh * c.T, Tu * 4);
+                            : make_rsrc(reinterpret_cast<const uint8_t*>(c.k_meta) + bh * c.T * kMt, Tu * kMt);
     const u32x4 rsp = SPARSE ? make_rsrc(c.k_sparse + bh * c.T * 2, Tu * 8) : rvm;
     const u32x4 rq = make_rsrc(q + ((size_t)b * p.Hq + (size_t)h * G) * kD, G * kD * 2);
     uint32_t koff = (uint32_t)tw0 * Gm::kRowK + lane * 16;
     uint32_t voff = (uint32_t)(tw0 / kBlock) * Gm::kV + lane * 16;
     uint32_t moff, mstep;
     if (mkind == 0) {
-      moff = (uint32_t)tw0 * 4 + lane * 16;
-      mstep = 4 * kBlock * 4;
+      moff = (uint32_t)tw0 * kMt + lane * 16;
+      mstep = 4 * kBlock * kMt;
     } else if (mkind == 1) {
-      moff = (KAXIS ? (uint32_t)(tw0 / kBlock) * kD * 4 : (uint32_t)tw0 * 4) + (lane - 8) * 16;
-      mstep = KAXIS ? 4 * kD * 4 : 4 * kBlock * 4;
+      moff = (KAXIS ? (uint32_t)(tw0 / kBlock) * kD * 4 : (uint32_t)tw0 * kMt) + (lane - Gm::kVm / 16) * 16;
+      mstep = KAXIS ? 4 * kD * 4 : 4 * kBlock * kMt;
     } else {
-      moff = (uint32_t)tw0 * 8 + (uint32_t)(lane - 8 - Gm::kKm / 16) * 16;
+      moff = (uint32_t)tw0 * 8 + (uint32_t)(lane - (Gm::kVm + Gm::kKm) / 16) * 16;
       mstep = 4 * kBlock * 8;
     }
 
@@ -586,8 +645,12 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
 #pragma unroll
       for (int x = 0; x < Gm::kV / 1024; ++x) dma16(rv, voff + x * 1024, lb + Gm::kK + x * 1024);
       const uint32_t lbm = lb + Gm::kK + Gm::kV;
-      if (mkind == 0) dma16(rvm, moff, lbm);
-      if (mkind == 1) dma16(rkm, moff, lbm);
+      if constexpr (Gm::kVm > 0) {
+        if (mkind == 0) dma16(rvm, moff, lbm);
+      }
+      if constexpr (Gm::kKm > 0) {
+        if (mkind == 1) dma16(rkm, moff, lbm);
+      }
       if constexpr (SPARSE) {
         if (mkind == 2 && lane < Gm::kMetaLanes) dma16(rsp, moff, lbm);
       }
@@ -610,9 +673,10 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     }
     float qv0[KAXIS ? G : 1], qv1[KAXIS ? G : 1];
     // token axis: the B operand is the raw fp16 query of head n mod G (exact);
-    // qsum_u = unit * sum_c q_c for the zero-point term
+    // qsum_u = unit * sum_c q_c for the zero-point term (symmetric blocks: the
+    // sum over each block's channels, qsum_b[j])
     Frag qfrag[KAXIS ? 1 : 4];
-    float qsum_u = 0.f;
+    float qsum_u = 0.f, qsum_b[kSym ? kSymBlocks : 1];
     if constexpr (KAXIS) {
       const float qs = qscale * (float)(1 << (kShK - bsh));
 #pragma unroll
@@ -624,13 +688,19 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
       float sum = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        float sj = 0.f;
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
-          const int ch0 = key_channel<KB>(grp, j, pp, 0), ch1 = key_channel<KB>(grp, j, pp, 1);
+          // symmetric blocks: MFMA j covers channel block j (lane group and
+          // chunk roles swapped)
+          const int ch0 = kSym ? key_channel<KB>(j, grp, pp, 0) : key_channel<KB>(grp, j, pp, 0);
+          const int ch1 = kSym ? key_channel<KB>(j, grp, pp, 1) : key_channel<KB>(grp, j, pp, 1);
           const uint32_t a0 = qlds[hq * kD + ch0], a1 = qlds[hq * kD + ch1];
           qfrag[j].p[pp] = a0 | (a1 << 16);
-          sum += h2f((uint16_t)a0) + h2f((uint16_t)a1);
+          sj += h2f((uint16_t)a0) + h2f((uint16_t)a1);
         }
+        if constexpr (kSym) qsum_b[j] = grp_sum(sj) * kUnitK;
+        sum += sj;
       }
       qsum_u = grp_sum(sum) * kUnitK;
     }
@@ -639,15 +709,19 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
 
     float m_ref = -INFINITY, l_run = 0.f;
     int vE = 0;                       // exponent the value-scale factor is set for
-    f4v acc[8], accz = {0.f, 0.f, 0.f, 0.f};
+    f4v acc[8], accz[kPB];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int z = 0; z < kPB; ++z) accz[z] = f4v{0.f, 0.f, 0.f, 0.f};
 
     // ---- scores of one tile -> online softmax -> P.V ---------------------------
     // sc[4e + r] is the scaled score (log2 units = sc * cs) of token
-    // 8grp + 4e + r; vm[i] the value meta of token 8grp + i; vcl/vch[j] the
-    // lane's value code words of channel chunk j.
-    auto softmax_pv = [&](float (&sc)[8], float cs, const uint32_t (&vm)[8], const uint32_t (&vcl)[8],
+    // 8grp + 4e + r; vm the value meta of tokens 8grp .. 8grp + 7 (affine: one
+    // word each; symmetric blocks: words 2i, 2i + 1 of token i, the scales of
+    // blocks 0, 1 and 2, 3; fp8: none); vcl/vch[j] the lane's value code
+    // words of channel chunk j.
+    auto softmax_pv = [&](float (&sc)[8], float cs, const uint32_t (&vm)[kVmW], const uint32_t (&vcl)[8],
                           const uint32_t (&vch)[8], int t0, int tend) {
       const int nvalid = tend - t0;
       if (nvalid < kBlock) {
@@ -667,52 +741,101 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) acc[j][r] *= ar[r];
-          accz[r] *= ar[r];
+#pragma unroll
+          for (int z = 0; z < kPB; ++z) accz[z][r] *= ar[r];
         }
         l_run *= alpha;
         m_ref = m_new;
       }
-      // value-scale exponent: raise it when a scale of this tile reaches 2^6 * 2^-kv
-      const uint16_t smax =
-          umax16(umax16(umax16((uint16_t)vm[0], (uint16_t)vm[1]), umax16((uint16_t)vm[2], (uint16_t)vm[3])),
-                 umax16(umax16((uint16_t)vm[4], (uint16_t)vm[5]), umax16((uint16_t)vm[6], (uint16_t)vm[7])));
-      if (__builtin_amdgcn_ballot_w64(smax >= (uint16_t)((vE + 1) << 10))) {
-        uint32_t sm = smax;
-        sm = max(sm, (uint32_t)__shfl_xor((int)sm, 16, 64));
-        sm = max(sm, (uint32_t)__shfl_xor((int)sm, 32, 64));
-        const int e_new = max(vE, (int)__builtin_amdgcn_readfirstlane(sm >> 10));
-        const float f = __builtin_bit_cast(float, (uint32_t)(127 + vE - e_new) << 23);
+      if constexpr (!kFp8) {
+        // value-scale exponent: raise it when a scale of this tile reaches 2^6 * 2^-kv
+        uint16_t smax;
+        if constexpr (kSym) {  // both halves of every word are scales
+          uint16_t m0 = 0, m1 = 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[j][r] *= f;
-          accz[r] *= f;
+          for (int i = 0; i < kVmW; ++i) {
+            m0 = umax16(m0, (uint16_t)vm[i]);
+            m1 = umax16(m1, (uint16_t)(vm[i] >> 16));
+          }
+          smax = umax16(m0, m1);
+        } else {
+          smax = umax16(umax16(umax16((uint16_t)vm[0], (uint16_t)vm[1]), umax16((uint16_t)vm[2], (uint16_t)vm[3])),
+                        umax16(umax16((uint16_t)vm[4], (uint16_t)vm[5]), umax16((uint16_t)vm[6], (uint16_t)vm[7])));
         }
-        l_run *= f;
-        vE = e_new;
+        if (__builtin_amdgcn_ballot_w64(smax >= (uint16_t)((vE + 1) << 10))) {
+          uint32_t sm = smax;
+          sm = max(sm, (uint32_t)__shfl_xor((int)sm, 16, 64));
+          sm = max(sm, (uint32_t)__shfl_xor((int)sm, 32, 64));
+          const int e_new = max(vE, (int)__builtin_amdgcn_readfirstlane(sm >> 10));
+          const float f = __builtin_bit_cast(float, (uint32_t)(127 + vE - e_new) << 23);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j][r] *= f;
+#pragma unroll
+            for (int z = 0; z < kPB; ++z) accz[z][r] *= f;
+          }
+          l_run *= f;
+          vE = e_new;
+        }
       }
-      const float kvm = (float)(kKvTop - vE) - m_ref;
-      // P = p * s * 2^kv; lo rows keep P - fp16(P)
-      float a[8];
+      // fp8: P = p (at most 2^kLazy); otherwise P = p * s * 2^kv
+      const float kvm = (kFp8 ? 0.f : (float)(kKvTop - vE)) - m_ref;
+      float x[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cs, kvm));
-        l_run += x;
-        a[i] = mul_lo(x, vm[i]);
+        x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cs, kvm));
+        l_run += x[i];
       }
-      Frag pf, bz;
+      // the P operand from the 8 weights a[] of the lane's tokens; lo rows keep
+      // P - fp16(P)
+      auto p_frag = [&](const float (&a)[8]) {
+        Frag pf;
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const int i0 = kPermV ? pp : 2 * pp;
-        const int i1 = kPermV ? pp + 4 : 2 * pp + 1;
-        const uint32_t hi = pk_rtz(a[i0], a[i1]);
-        pf.p[pp] = pk_rtz(__builtin_fmaf(f16lo(hi), -rowlo, a[i0]), __builtin_fmaf(f16hi(hi), -rowlo, a[i1]));
-        // (z'_i0, z'_i1) in code steps, z' = z - qmin
-        bz.p[pp] = pk_fma16(perm(vm[i1], vm[i0], 0x07060302u), h2v{kZv, kZv}, h2v{kZvOfs, kZvOfs});
+        for (int pp = 0; pp < 4; ++pp) {
+          const int i0 = kPermV ? pp : 2 * pp;
+          const int i1 = kPermV ? pp + 4 : 2 * pp + 1;
+          const uint32_t hi = pk_rtz(a[i0], a[i1]);
+          pf.p[pp] = pk_rtz(__builtin_fmaf(f16lo(hi), -rowlo, a[i0]), __builtin_fmaf(f16hi(hi), -rowlo, a[i1]));
+        }
+        return pf;
+      };
+      if constexpr (kFp8) {
+        const Frag pf = p_frag(x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = mfma(pf, fp8_frag(vcl[j], vch[j]), acc[j]);
+      } else if constexpr (kSym) {
+        // channel chunk j (channels 16 j .. 16 j + 15) lies in block j / 2
+#pragma unroll
+        for (int bk = 0; bk < kSymBlocks; ++bk) {
+          float a[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t w2 = vm[2 * i + (bk >> 1)];
+            a[i] = __builtin_fmaf(x[i], (bk & 1) ? f16hi(w2) : f16lo(w2), 0.f);
+          }
+          const Frag pf = p_frag(a);
+          accz[bk] = mfma(pf, bsym, accz[bk]);
+          acc[2 * bk] = mfma(pf, val_frag<VB>(vcl[2 * bk], vch[2 * bk]), acc[2 * bk]);
+          acc[2 * bk + 1] = mfma(pf, val_frag<VB>(vcl[2 * bk + 1], vch[2 * bk + 1]), acc[2 * bk + 1]);
+        }
+      } else {
+        float a[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = mul_lo(x[i], vm[i]);
+        const Frag pf = p_frag(a);
+        Frag bz;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const int i0 = kPermV ? pp : 2 * pp;
+          const int i1 = kPermV ? pp + 4 : 2 * pp + 1;
+          // (z'_i0, z'_i1) in code steps, z' = z - qmin
+          bz.p[pp] = pk_fma16(perm(vm[i1], vm[i0], 0x07060302u), h2v{kZv, kZv}, h2v{kZvOfs, kZvOfs});
+        }
+        accz[0] = mfma(pf, bz, accz[0]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = mfma(pf, val_frag<VB>(vcl[j], vch[j]), acc[j]);
       }
-      accz = mfma(pf, bz, accz);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = mfma(pf, val_frag<VB>(vcl[j], vch[j]), acc[j]);
     };
 
     // the B operand of the key product for a block: scaled query (hi/lo) with
@@ -741,27 +864,47 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
       const uint8_t* kbuf = sb;
       const uint8_t* vbuf = sb + Gm::kK;
       const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(sb + Gm::kK + Gm::kV);
-      const uint32_t* kmeta = vmeta + 32;
+      const uint32_t* kmeta = vmeta + Gm::kVm / 4;
       const uint32_t* spr = kmeta + Gm::kKm / 4;
       const int t0 = ts0 + (w + 4 * i) * kBlock;
 
-      uint32_t vm[8];
-      {
-        const uint4 a = reinterpret_cast<const uint4*>(vmeta + 8 * grp)[0];
-        const uint4 bb = reinterpret_cast<const uint4*>(vmeta + 8 * grp)[1];
-        vm[0] = a.x; vm[1] = a.y; vm[2] = a.z; vm[3] = a.w;
-        vm[4] = bb.x; vm[5] = bb.y; vm[6] = bb.z; vm[7] = bb.w;
+      // metadata words of the lane's tokens 8grp .. 8grp + 7 (kVmW per array)
+      uint32_t vm[kVmW];
+      if constexpr (!kFp8) {
+#pragma unroll
+        for (int x = 0; x < kVmW / 4; ++x) {
+          const uint4 a = reinterpret_cast<const uint4*>(vmeta + kVmW * grp)[x];
+          vm[4 * x] = a.x; vm[4 * x + 1] = a.y; vm[4 * x + 2] = a.z; vm[4 * x + 3] = a.w;
+        }
       }
       // key codes of the lane's two A rows: bytes [grp*4KB, +4KB) of each row
-      uint32_t kc[2][KB];
+      // (symmetric blocks: kc[e][j] / kc[e][2j, 2j+1] the words sym_key_frag
+      // takes for block j)
+      uint32_t kc[2][kSym ? (KB == 8 ? 8 : 4) : KB];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const uint8_t* row = kbuf + a_token(e, c16) * Gm::kRowK + grp * 4 * KB;
+        const uint8_t* rowb = kbuf + a_token(e, c16) * Gm::kRowK;
+        if constexpr (kSym) {
 #pragma unroll
-        for (int x = 0; x < KB; x += 2) {
-          const uint2 y = reinterpret_cast<const uint2*>(row)[x / 2];
-          kc[e][x] = y.x;
-          kc[e][x + 1] = y.y;
+          for (int j = 0; j < 4; ++j) {
+            if constexpr (KB == 8) {
+              const uint2 y = reinterpret_cast<const uint2*>(rowb + 32 * j + 8 * grp)[0];
+              kc[e][2 * j] = y.x;
+              kc[e][2 * j + 1] = y.y;
+            } else if constexpr (KB == 4) {
+              kc[e][j] = reinterpret_cast<const uint32_t*>(rowb + 16 * j + 4 * grp)[0];
+            } else {
+              kc[e][j] = reinterpret_cast<const uint32_t*>(rowb + 8 * j + 4 * (grp >> 1))[0] >> (8 * (grp & 1));
+            }
+          }
+        } else {
+          const uint8_t* row = rowb + grp * 4 * KB;
+#pragma unroll
+          for (int x = 0; x < KB; x += 2) {
+            const uint2 y = reinterpret_cast<const uint2*>(row)[x / 2];
+            kc[e][x] = y.x;
+            kc[e][x + 1] = y.y;
+          }
         }
       }
       float sc[8];
@@ -784,6 +927,47 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
 #pragma unroll
           for (int r = 0; r < 4; ++r) sc[4 * e + r] = add_ror<G>(s[e][r]);
         cs = kInvUnitK;
+      } else if constexpr (kFp8) {
+        // keys are E4M3 values times the cache's key scale
+        f4v s[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) s[e] = mfma(fp8_frag(kc[e][2 * j], kc[e][2 * j + 1]), qfrag[j], s[e]);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[4 * e + r] = s[e][r];
+        cs = qscale * c.kscale;
+      } else if constexpr (kSym) {
+        // one product per 32-channel block (its scale differs per token),
+        // seeded with q_min * sum of the block's query channels; then
+        // score = sum_j s_j(t) * block product j
+        uint32_t km[16];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const uint4 a = reinterpret_cast<const uint4*>(kmeta + 16 * grp)[x];
+          km[4 * x] = a.x; km[4 * x + 1] = a.y; km[4 * x + 2] = a.z; km[4 * x + 3] = a.w;
+        }
+#pragma unroll
+        for (int i2 = 0; i2 < 8; ++i2) sc[i2] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float seed = (float)kQMinK * qsum_b[j];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            Frag kf;
+            if constexpr (KB == 8) kf = sym_key_frag<KB>(kc[e][2 * j], kc[e][2 * j + 1]);
+            else kf = sym_key_frag<KB>(kc[e][j], 0u);
+            const f4v sj = mfma(kf, qfrag[j], f4v{seed, seed, seed, seed});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t kw = km[2 * (4 * e + r) + (j >> 1)];
+              sc[4 * e + r] = __builtin_fmaf(sj[r], (j & 1) ? f16hi(kw) : f16lo(kw), sc[4 * e + r]);
+            }
+          }
+        }
+        cs = kInvUnitK * qscale;
       } else {
         uint32_t km[8];
         {
@@ -885,7 +1069,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
             sc[r] = (e == 0) ? v : -INFINITY;
             sc[4 + r] = (e == 0) ? -INFINITY : v;
           }
-          uint32_t vm[8], vcl[8], vch[8];
+          uint32_t vm[kVmW], vcl[8], vch[8];
           {
             const uint4 a = reinterpret_cast<const uint4*>(vmres_lds + 8 * grp)[0];
             const uint4 bb = reinterpret_cast<const uint4*>(vmres_lds + 8 * grp)[1];
@@ -902,9 +1086,10 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     }
 
     // ---- merge the wavefronts of the workgroup ------------------------------
-    // o = (acc - accz) / (value code unit) * 2^-kv, l = l_run * 2^-kv
-    const float ofac = __builtin_bit_cast(float, (uint32_t)(127 + 24 - kShV - kKvTop + vE) << 23);
-    const float lfac = __builtin_bit_cast(float, (uint32_t)(127 - kKvTop + vE) << 23);
+    // o = (acc - accz) / (value code unit) * 2^-kv, l = l_run * 2^-kv; fp8:
+    // o = acc * (value scale), l = l_run
+    const float ofac = kFp8 ? c.vscale : __builtin_bit_cast(float, (uint32_t)(127 + 24 - kShV - kKvTop + vE) << 23);
+    const float lfac = kFp8 ? 1.f : __builtin_bit_cast(float, (uint32_t)(127 - kKvTop + vE) << 23);
     const float lsum = grp_sum(l_run) * lfac;
     wait_vm<0>();     // no tile load still writing LDS
     __syncthreads();  // every wavefront is done with its slots
@@ -918,7 +1103,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * grp + r;
-        if (row < 2 * G) mg.o[w][row][16 * j + c16] = (acc[j][r] - accz[r]) * ofac;
+        if (row < 2 * G) mg.o[w][row][16 * j + c16] = (kFp8 ? acc[j][r] : acc[j][r] - accz[kSym ? j / 2 : 0][r]) * ofac;
       }
     __syncthreads();
     for (int e = tid; e < G * kD; e += 256) {
@@ -1024,12 +1209,12 @@ __global__ __launch_bounds__(128) void combine_kernel(CacheView c, AttnPlan p, c
 
 // Launch of one kernel variant, or (occ != nullptr) its resident workgroups
 // per compute unit.
-template <int KB, int VB, int KAXIS, int G, bool SPARSE>
+template <int KB, int VB, int KAXIS, int G, bool SPARSE, int FMT>
 hipError_t launch_t(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
                     hipStream_t st, int* occ) {
   if (occ) {
-    const void* fn = reinterpret_cast<const void*>(attn_kernel<KB, VB, KAXIS, G, SPARSE>);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, attn_kernel<KB, VB, KAXIS, G, SPARSE>, 256, 0) ==
+    const void* fn = reinterpret_cast<const void*>(attn_kernel<KB, VB, KAXIS, G, SPARSE, FMT>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, attn_kernel<KB, VB, KAXIS, G, SPARSE, FMT>, 256, 0) ==
             hipSuccess && *occ > 0)
       return hipSuccess;
     (void)hipGetLastError();  // the query is optional: do not leave its error behind
@@ -1048,49 +1233,65 @@ hipError_t launch_t(const CacheView& c, const AttnPlan& p, const uint16_t* q, fl
     return hipSuccess;
   }
   dim3 grid(p.n_wg);
-  hipLaunchKernelGGL((attn_kernel<KB, VB, KAXIS, G, SPARSE>), grid, dim3(256), 0, st, c, p, q, out, ws);
+  hipLaunchKernelGGL((attn_kernel<KB, VB, KAXIS, G, SPARSE, FMT>), grid, dim3(256), 0, st, c, p, q, out, ws);
   return hipGetLastError();
 }
 
-template <int KB, int VB, int KAXIS, bool SPARSE>
+template <int KB, int VB, int KAXIS, bool SPARSE, int FMT>
 hipError_t dispatch_g(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
                       hipStream_t st, int* occ) {
   switch (p.group) {
-    case 1: return launch_t<KB, VB, KAXIS, 1, SPARSE>(c, p, q, out, ws, st, occ);
-    case 2: return launch_t<KB, VB, KAXIS, 2, SPARSE>(c, p, q, out, ws, st, occ);
-    case 4: return launch_t<KB, VB, KAXIS, 4, SPARSE>(c, p, q, out, ws, st, occ);
-    case 8: return launch_t<KB, VB, KAXIS, 8, SPARSE>(c, p, q, out, ws, st, occ);
+    case 1: return launch_t<KB, VB, KAXIS, 1, SPARSE, FMT>(c, p, q, out, ws, st, occ);
+    case 2: return launch_t<KB, VB, KAXIS, 2, SPARSE, FMT>(c, p, q, out, ws, st, occ);
+    case 4: return launch_t<KB, VB, KAXIS, 4, SPARSE, FMT>(c, p, q, out, ws, st, occ);
+    case 8: return launch_t<KB, VB, KAXIS, 8, SPARSE, FMT>(c, p, q, out, ws, st, occ);
   }
   return hipErrorInvalidValue;
 }
 
-template <int KB, int VB>
+// affine codes: keys on either axis (channel axis with or without sparse
+// entries); symmetric blocks: token axis
+template <int KB, int VB, int FMT>
 hipError_t dispatch_axis(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
                          hipStream_t st, int* occ) {
-  if (c.kaxis == 0) return dispatch_g<KB, VB, 0, false>(c, p, q, out, ws, st, occ);
-  if (c.sparse) return dispatch_g<KB, VB, 1, true>(c, p, q, out, ws, st, occ);
-  return dispatch_g<KB, VB, 1, false>(c, p, q, out, ws, st, occ);
+  if (c.kaxis == 0) return dispatch_g<KB, VB, 0, false, FMT>(c, p, q, out, ws, st, occ);
+  if constexpr (FMT == kFmtInt) {
+    if (c.sparse) return dispatch_g<KB, VB, 1, true, FMT>(c, p, q, out, ws, st, occ);
+    return dispatch_g<KB, VB, 1, false, FMT>(c, p, q, out, ws, st, occ);
+  }
+  return hipErrorInvalidValue;
 }
 
-template <int KB>
+template <int KB, int FMT>
 hipError_t dispatch_vb(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
                        hipStream_t st, int* occ) {
   switch (c.vbits) {
-    case 8: return dispatch_axis<KB, 8>(c, p, q, out, ws, st, occ);
-    case 4: return dispatch_axis<KB, 4>(c, p, q, out, ws, st, occ);
-    case 2: return dispatch_axis<KB, 2>(c, p, q, out, ws, st, occ);
+    case 8: return dispatch_axis<KB, 8, FMT>(c, p, q, out, ws, st, occ);
+    case 4: return dispatch_axis<KB, 4, FMT>(c, p, q, out, ws, st, occ);
+    case 2: return dispatch_axis<KB, 2, FMT>(c, p, q, out, ws, st, occ);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int FMT>
+hipError_t dispatch_kb(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
+                       hipStream_t st, int* occ) {
+  switch (c.kbits) {
+    case 8: return dispatch_vb<8, FMT>(c, p, q, out, ws, st, occ);
+    case 4: return dispatch_vb<4, FMT>(c, p, q, out, ws, st, occ);
+    case 2: return dispatch_vb<2, FMT>(c, p, q, out, ws, st, occ);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t dispatch(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
                     hipStream_t st, int* occ) {
-  switch (c.kbits) {
-    case 8: return dispatch_vb<8>(c, p, q, out, ws, st, occ);
-    case 4: return dispatch_vb<4>(c, p, q, out, ws, st, occ);
-    case 2: return dispatch_vb<2>(c, p, q, out, ws, st, occ);
+  if (c.fmt == kFmtFp8) {  // 8-bit keys and values, token axis
+    if (c.kbits != 8 || c.vbits != 8 || c.kaxis != 0) return hipErrorInvalidValue;
+    return dispatch_g<8, 8, 0, false, kFmtFp8>(c, p, q, out, ws, st, occ);
   }
-  return hipErrorInvalidValue;
+  if (c.fmt == kFmtSym32) return dispatch_kb<kFmtSym32>(c, p, q, out, ws, st, occ);
+  return dispatch_kb<kFmtInt>(c, p, q, out, ws, st, occ);
 }
 
 }  // namespace
@@ -1109,13 +1310,13 @@ hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p, const 
 int attention_blocks_per_cu(const CacheView& c, int group) {
   // cached per device and kernel variant (0 = not queried yet; threads may
   // race to fill an entry with the same value)
-  static std::atomic<int> cache[16][3][3][2][2][4];
+  static std::atomic<int> cache[16][3][3][2][2][4][3];
   const auto bi = [](int b) { return b == 2 ? 0 : (b == 4 ? 1 : 2); };
   const int gi = group == 1 ? 0 : (group == 2 ? 1 : (group == 4 ? 2 : 3));
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = -1;
   std::atomic<int>* slot =
-      dev >= 0 ? &cache[dev][bi(c.kbits)][bi(c.vbits)][c.kaxis ? 1 : 0][c.sparse ? 1 : 0][gi] : nullptr;
+      dev >= 0 ? &cache[dev][bi(c.kbits)][bi(c.vbits)][c.kaxis ? 1 : 0][c.sparse ? 1 : 0][gi][c.fmt % 3] : nullptr;
   if (slot) {
     const int known = slot->load(std::memory_order_relaxed);
     if (known > 0) return known;

@@ -2,7 +2,8 @@
 //
 // x_hat = scale * (q - zero_point) ("KV Cache Quantization — 8-bit and 4-bit",
 // "Integer quantization in one screen"), exact in fp32 and rounded once to
-// fp16. This materializing pass is what the attention kernel avoids ("Decode
+// fp16; symmetric blocks x_hat = s * q (exact in fp32); fp8 x_hat = scale *
+// value(code), the fp32 product rounded to fp16. This materializing pass is what the attention kernel avoids ("Decode
 // is memory-bound, so smaller is also faster"); it exists for checking and
 // for callers that need plain fp16 tensors.
 #include "kvq_device.h"
@@ -10,6 +11,19 @@
 namespace kvq {
 
 namespace {
+
+// fp32 reconstruction of element ch of token t (code u) for a token-axis cache
+// side: meta points at that side's metadata array.
+__device__ __forceinline__ float token_elem(const CacheView& c, uint32_t u, const uint32_t* meta, size_t tok,
+                                           int ch, int bits, float scale) {
+#pragma clang fp contract(off)
+  if (c.fmt == kFmtFp8) return scale * e4m3_value(u);
+  if (c.fmt == kFmtSym32) {
+    const float s = h2f(reinterpret_cast<const uint16_t*>(meta)[tok * kSymBlocks + ch / 32]);
+    return s * (float)((int)u + qmin_of(bits));
+  }
+  return dequant(u, meta[tok], bits);
+}
 
 // One workgroup per (32-token block, KV head, sequence); thread -> (token,
 // 16 channels).
@@ -32,9 +46,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(CacheView c, uint16_t* kou
   for (int ch = c0; ch < c0 + 16; ++ch) {
     uint16_t kh = 0, vh = 0;
     if (t < Q) {
-      const uint32_t meta = c.kaxis == 0 ? c.k_meta[bh * c.T + t]
-                                         : c.k_meta[(bh * (c.T / kBlock) + j) * kD + ch];
-      float x = dequant(get_field(krow, ch, c.kbits), meta, c.kbits);
+      const uint32_t u = get_field(krow, ch, c.kbits);
+      float x = c.kaxis == 0 ? token_elem(c, u, c.k_meta, bh * c.T + t, ch, c.kbits, c.kscale)
+                             : dequant(u, c.k_meta[(bh * (c.T / kBlock) + j) * kD + ch], c.kbits);
       if ((sp_col & 0xFFFFu) == (uint32_t)ch) x = x + h2f((uint16_t)(sp_val & 0xFFFFu));
       if ((sp_col >> 16) == (uint32_t)ch) x = x + h2f((uint16_t)(sp_val >> 16));
       kh = f2h_rne(x);
@@ -42,8 +56,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(CacheView c, uint16_t* kou
       kh = c.k_resid[(bh * c.R + (t - Q)) * kD + ch];
     }
     if (t < L) {
-      const float x = dequant(get_field(vblk + ch * 4 * c.vbits, tau, c.vbits),
-                              c.v_meta[bh * c.T + t], c.vbits);
+      const float x = token_elem(c, get_field(vblk + ch * 4 * c.vbits, tau, c.vbits), c.v_meta, bh * c.T + t,
+                                 ch, c.vbits, c.vscale);
       vh = f2h_rne(x);
     }
     kout[o + ch] = kh;

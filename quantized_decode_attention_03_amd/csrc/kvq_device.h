@@ -84,6 +84,66 @@ __device__ __forceinline__ float dequant(uint32_t u, uint32_t meta, int bits) {
   return s * ((float)((int)u + qmin_of(bits)) - z);
 }
 
+// ---- fp8 E4M3 elements (OCP layout: sign bit 7, exponent bits 6..3 with
+// bias 7, mantissa bits 2..0; exponent field 0 holds the subnormals m * 2^-9;
+// S.1111.111 is NaN, so the largest finite magnitude is 448) ----------------
+
+// Code of an fp32 value: the nearest E4M3 magnitude, ties to the even code,
+// magnitudes at or above 448 saturated to 448, the sign kept (a negative value
+// that rounds to zero gives 0x80). Finite inputs.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t bits = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t ab = bits & 0x7FFFFFFFu;
+  const float a = __builtin_bit_cast(float, ab);
+  uint32_t c;
+  if (a >= 448.0f) {
+    c = 0x7Eu;
+  } else if (a < 0.015625f) {
+    // subnormal range (below 2^-6): steps of 2^-9; rint ties to even, and the
+    // even integer is the even code (8 becomes the smallest normal, 2^-6)
+    c = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    // normal: keep 3 of the 23 fp32 mantissa bits, rounding to nearest even
+    // on the integer bit pattern (a carry moves into the exponent), then
+    // rebias the exponent from 127 to 7
+    const uint32_t r = ab + 0x7FFFFu + ((ab >> 20) & 1u);
+    c = (r >> 20) - ((127u - 7u) << 3);
+  }
+  return c | sign;
+}
+
+// Exact fp32 value of an E4M3 code (NaN for S.1111.111).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  float v;
+  if (e == 0xFu && m == 7u) {
+    v = __builtin_nanf("");
+  } else if (e == 0) {
+    v = (float)m * 0.001953125f;  // m * 2^-9
+  } else {
+    v = __builtin_bit_cast(float, ((e + 127u - 7u) << 23) | (m << 20));
+  }
+  return (c & 0x80u) ? -v : v;
+}
+
+// ---- symmetric blocks: x_hat = s * q, q in [-q_max, q_max] ----------------
+
+// Block scale: the smallest fp16 >= max|x| / q_max, 1.0 for an all-zero block.
+__device__ __forceinline__ uint16_t sym_scale16(float amax, int bits) {
+#pragma clang fp contract(off)
+  if (amax == 0.0f) return (uint16_t)0x3C00;
+  return f2h_up(amax / (float)qmax_of(bits));
+}
+
+// Stored code u = q - q_min of one element of a block with scale s.
+__device__ __forceinline__ uint32_t sym_code(float x, float s, int bits) {
+#pragma clang fp contract(off)
+  const float qm = (float)qmax_of(bits);
+  const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(x / s), -qm), qm);
+  return (uint32_t)((int)q - qmin_of(bits));
+}
+
 // b-bit field i of a little-endian packed byte array.
 __device__ __forceinline__ uint32_t get_field(const uint8_t* p, int i, int bits) {
   const int bit = i * bits;

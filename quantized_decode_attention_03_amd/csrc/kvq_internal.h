@@ -11,6 +11,12 @@ namespace kvq {
 constexpr int kD = 128;      // channels per head
 constexpr int kBlock = 32;   // tokens per key group / value code block
 
+// Element formats (keys and values alike): affine integer codes with scale
+// and zero point, fp8 E4M3 bytes with one scale per cache side, or symmetric
+// codes with one fp16 scale per 32-channel block of a token.
+enum : int { kFmtInt = 0, kFmtFp8 = 1, kFmtSym32 = 2 };
+constexpr int kSymBlocks = 4;  // 32-channel blocks per token vector
+
 // Everything a kernel needs to address one layer's cache.
 struct CacheView {
   int B, H, T;                 // batch, KV heads, capacity (multiple of 32)
@@ -18,6 +24,8 @@ struct CacheView {
   int kaxis;                   // 0 token, 1 channel
   int R;                       // residual slots (channel axis), else 0
   int sparse;                  // entries per key vector in k_sparse (0 or 2)
+  int fmt;                     // kFmt*: element format of keys and values
+  float kscale, vscale;        // fp8: per-cache scales (x_hat = scale * value)
   uint8_t* k_codes;
   uint32_t* k_meta;
   uint16_t* k_resid;

@@ -47,6 +47,9 @@ class Spec:
     steps: int               # decode steps (append 1 token + attend)
     seed: int
     d_head: int = 128
+    fmt: str = "int"         # element format: "int" (affine), "fp8" or "sym32"
+    k_scale: float = 1.0     # fp8 per-cache scales
+    v_scale: float = 1.0
 
     @property
     def ragged(self):

@@ -13,7 +13,8 @@ ATOL = 2e-3   # attention tolerance, max-abs against the float64 oracle
 
 def ref_config(s):
     return RefConfig(s.d_head, s.n_kv_heads, s.n_q_heads, s.k_bits, s.v_bits, s.k_axis,
-                     s.k_group, s.k_residual, s.k_sparse)
+                     s.k_group, s.k_residual, s.k_sparse, k_format=s.fmt, v_format=s.fmt,
+                     k_scale=s.k_scale, v_scale=s.v_scale)
 
 
 def to_dev(a):
@@ -79,8 +80,14 @@ class Pair:
         out = {
             "k_codes": g.k_codes.cpu().numpy().reshape(B, H, T, D * s.k_bits // 8),
             "v_codes": g.v_codes.cpu().numpy().reshape(B, H, T // 32, D, 4 * s.v_bits),
-            "v_meta": g.v_meta.cpu().numpy().view(np.uint32).reshape(B, H, T),
         }
+        if s.fmt == "fp8":       # no metadata arrays
+            return out
+        if s.fmt == "sym32":     # fp16 block scales [B, H, T, 4]
+            out["v_meta"] = g.v_meta.cpu().numpy().view(np.uint16).reshape(B, H, T, 4)
+            out["k_meta"] = g.k_meta.cpu().numpy().view(np.uint16).reshape(B, H, T, 4)
+            return out
+        out["v_meta"] = g.v_meta.cpu().numpy().view(np.uint32).reshape(B, H, T)
         if s.k_axis == "channel":
             out["k_meta"] = g.k_meta.cpu().numpy().view(np.uint32).reshape(B, H, T // 32, D)
             out["k_resid"] = g.k_resid.cpu().numpy().view(np.uint16).reshape(B, H, s.k_residual, D)

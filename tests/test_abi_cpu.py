@@ -35,19 +35,40 @@ def _cfg(**kw):
     return Config(**base)
 
 
+TOKEN_AXIS = dict(k_axis="token", k_group_tokens=0, k_residual_tokens=0)
+
+
 def test_sizes_match_oracle_formula():
     from oracle import sizes
     from oracle.cache import Config as RC
     for kw in [dict(), dict(k_bits=2, v_bits=2, k_residual_tokens=128),
                dict(k_sparse_per_vector=2),
-               dict(k_axis="token", k_group_tokens=0, k_residual_tokens=0, k_bits=8, v_bits=8)]:
+               dict(TOKEN_AXIS, k_bits=8, v_bits=8),
+               dict(TOKEN_AXIS, k_bits=8, v_bits=8, k_format="fp8", k_scale=0.5, v_scale=2.0),
+               dict(TOKEN_AXIS, k_bits=8, v_bits=8, k_format="sym32"),
+               dict(TOKEN_AXIS, k_bits=4, v_bits=2, k_format="sym32")]:
         c = _cfg(**kw)
         got = kvq_cache_sizes(c, 3, 4096)
         rc = RC(128, c.n_kv_heads, c.n_q_heads, c.k_bits, c.v_bits, c.k_axis, c.k_group_tokens,
-                c.k_residual_tokens, c.k_sparse_per_vector)
+                c.k_residual_tokens, c.k_sparse_per_vector, k_format=c.k_format,
+                v_format=c.v_format, k_scale=c.k_scale, v_scale=c.v_scale)
         want = sizes.actual_bytes(rc, 3, 4096)
         for k, v in want.items():
-            assert got[k] == v, k
+            assert got[k] == v, (kw, k)
+
+
+def test_block_format_sizes_per_token():
+    # 8-bit caches: one byte per element plus, for the 32-element blocks, one
+    # fp16 scale per block (34 B per 32 elements, the 2 extra KiB per 64 KiB of
+    # the glossary's q8_0); fp8 carries no per-element metadata at all
+    D, H = 128, 8
+    per_tok = lambda c: (kvq_cache_sizes(c, 1, 4096)["total_bytes"] - 4) / 4096
+    fp8 = _cfg(**TOKEN_AXIS, k_bits=8, v_bits=8, k_format="fp8")
+    q8 = _cfg(**TOKEN_AXIS, k_bits=8, v_bits=8, k_format="sym32")
+    q4 = _cfg(**TOKEN_AXIS, k_bits=4, v_bits=4, k_format="sym32")
+    assert per_tok(fp8) == 2 * H * D
+    assert per_tok(q8) == 2 * H * D * 34 / 32
+    assert per_tok(q4) == 2 * H * D * 18 / 32
 
 
 def test_worked_example_nominal():
@@ -69,6 +90,14 @@ def test_worked_example_nominal():
     (dict(k_group_tokens=64), N.KVQ_EUNSUPPORTED),
     (dict(k_sparse_per_vector=3), N.KVQ_EUNSUPPORTED),
     (dict(k_axis="token"), N.KVQ_EINVAL),
+    # formats: fp8 is 8-bit, token axis; one format for keys and values
+    (dict(TOKEN_AXIS, k_format="fp8"), N.KVQ_EINVAL),
+    (dict(k_bits=8, v_bits=8, k_format="fp8"), N.KVQ_EUNSUPPORTED),
+    (dict(k_format="sym32"), N.KVQ_EUNSUPPORTED),
+    (dict(TOKEN_AXIS, k_format="sym32", v_format="int"), N.KVQ_EUNSUPPORTED),
+    (dict(TOKEN_AXIS, k_bits=8, v_bits=8, k_format="fp8", k_scale=0.0), N.KVQ_EINVAL),
+    (dict(TOKEN_AXIS, k_bits=8, v_bits=8, k_format="fp8", v_scale=float("inf")), N.KVQ_EINVAL),
+    (dict(TOKEN_AXIS, k_bits=8, v_bits=8, k_format="fp8", v_scale=float("nan")), N.KVQ_EINVAL),
 ])
 def test_bad_config(kw, status):
     c = _cfg(**kw)
@@ -76,6 +105,29 @@ def test_bad_config(kw, status):
         kvq_cache_sizes(c, 2, 256)
     assert e.value.status == status
     assert kvq_workspace_bytes(c, 2, 256) == 0
+
+
+def test_unknown_format_code():
+    c = _cfg(**TOKEN_AXIS).c()
+    c.k_format = c.v_format = 7
+    out = N.kvq_sizes()
+    assert N.lib().kvq_cache_sizes(ctypes.byref(c), 2, 256, ctypes.byref(out)) == N.KVQ_EINVAL
+
+
+def test_fp8_cache_needs_no_meta_pointers():
+    L = N.lib()
+    pc = _cfg(**TOKEN_AXIS, k_bits=8, v_bits=8, k_format="fp8")
+    cfg = pc.c()
+    c, lh = _fake_cache(pc, 2, 64, [60, 0])
+    c.k_meta = c.v_meta = None
+    cu = ctypes.cast(ctypes.c_void_p(1 << 20), ctypes.POINTER(ctypes.c_int32))
+    fake = ctypes.c_void_p(1 << 20)
+    n = (ctypes.c_int32 * 2)(5, 1)               # reaches the capacity check: the cache itself is valid
+    assert L.kvq_append(ctypes.byref(cfg), ctypes.byref(c), fake, fake, cu, n, None) == N.KVQ_ECAPACITY
+    # an affine cache without metadata is invalid
+    pi = _cfg(**TOKEN_AXIS, k_bits=8, v_bits=8)
+    ci = pi.c()
+    assert L.kvq_append(ctypes.byref(ci), ctypes.byref(c), fake, fake, cu, n, None) == N.KVQ_EINVAL
 
 
 def _fake_cache(cfg, batch, max_tokens, lens):
