@@ -45,14 +45,17 @@ def algorithmic_bytes(s, lens):
     the fp32 outputs. Per (sequence, KV head) with L tokens of which Q are
     quantized keys."""
     H, D = s.n_kv_heads, s.d_head
+    # metadata bytes per token of a token-axis side: one word (affine codes),
+    # four fp16 block scales (symmetric blocks), none (fp8)
+    meta_tok = {"int": 4, "sym32": 8, "fp8": 0}[s.fmt]
     tot = 0
     for L in lens:
         Q = L if s.k_axis == "token" else L - L % s.k_residual
         k = Q * D * s.k_bits // 8
-        k += (Q // 32) * D * 4 if s.k_axis == "channel" else Q * 4
+        k += (Q // 32) * D * 4 if s.k_axis == "channel" else Q * meta_tok
         k += (L - Q) * D * 2
         k += Q * 8 if s.k_sparse else 0
-        v = L * D * s.v_bits // 8 + L * 4
+        v = L * D * s.v_bits // 8 + L * meta_tok
         tot += H * (k + v)
     tot += s.batch * s.n_q_heads * D * (2 + 4)
     return tot
@@ -189,14 +192,33 @@ def copy_probe():
 DEFAULT_WORKLOADS = (2, 4, 5)   # int4 KIVI, int2 KIVI, ragged int4 + sparse (headline: the largest)
 
 
-def run_workload(cid, args):
-    """Prefill, settle, warm up and time one workload; returns its result
-    entry (everything but the host baseline)."""
+def format_specs():
+    """The 8-bit per-token workload's shape (B=1, Hq=32, Hkv=8, S=32768), one
+    layer, in each element format: affine int8 (the workload's own), fp8 E4M3
+    with per-cache scales, and symmetric 32-channel blocks at 8 and 4 bits
+    (llama.cpp's q8_0 / q4_0 block shapes)."""
+    from dataclasses import replace
+    from quantized_decode_attention_03_amd import workloads as W
+    base = W.spec(3, layers=1)
+    shape = "B=1, Hq=32, Hkv=8, S=32768, one layer"
+    return [
+        (3, replace(base, name=f"int8 per-token K/V (affine), {shape}")),
+        ("3-fp8", replace(base, fmt="fp8", name=f"fp8 E4M3 K/V (per-cache scales 1.0), {shape}")),
+        ("3-sym8", replace(base, fmt="sym32", name=f"int8 symmetric 32-channel blocks K/V, {shape}")),
+        ("3-sym4", replace(base, fmt="sym32", k_bits=4, v_bits=4,
+                           name=f"int4 symmetric 32-channel blocks K/V, {shape}")),
+    ]
+
+
+def run_workload(key, args, s=None):
+    """Prefill, settle, warm up and time one workload (workload number key, or
+    the spec s recorded under key); returns its result entry (everything but
+    the host baseline)."""
     import torch
     import quantized_decode_attention_03_amd as K
     from quantized_decode_attention_03_amd import workloads as W
 
-    s = W.spec(cid)
+    s = W.spec(key) if s is None else s
     dev = "cuda"
     lens0 = [int(x) for x in W.seq_lengths(s)]
     cache_bytes = algorithmic_bytes(s, lens0)
@@ -220,7 +242,7 @@ def run_workload(cid, args):
     # prefills into fresh caches (quantize-on-append of the whole context);
     # the replicas are those caches and clones of the first; further layers
     # get caches of their own
-    progress(f"workload {s.cid}: generating {sum(lens0)} prefill tokens x {nlay} layer(s)")
+    progress(f"workload {key}: generating {sum(lens0)} prefill tokens x {nlay} layer(s)")
     kd, vd = prefill_inputs(0)
     base = K.KVCache(cfg, s.batch, T)
     K.kvq_append(base, kd, vd, cu, lens0)
@@ -326,20 +348,22 @@ def run_workload(cid, args):
     attn_avg_s = float(np.mean(attn_ms)) / 1e3
     bytes_avg = float(np.mean([algorithmic_bytes(s, L) for L in lens_timed]))
     achieved = bytes_avg / attn_avg_s / 1e9
-    progress(f"workload {s.cid}: {args.steps} timed steps in {wall:.3f} s, attention {attn_avg_s * 1e6:.1f} us")
+    progress(f"workload {key}: {args.steps} timed steps in {wall:.3f} s, attention {attn_avg_s * 1e6:.1f} us")
     return {
         "workload": s.name,
         "value": s.batch * args.steps / wall,
         "unit": "tokens/s",
         "ms_per_step": wall / args.steps * 1e3,
-        "dtype": f"f16 MFMA, f32 accumulate (int{s.k_bits}/int{s.v_bits} codes)",
+        "dtype": "f16 MFMA, f32 accumulate (" + (
+            "fp8 E4M3 codes" if s.fmt == "fp8" else
+            f"int{s.k_bits}/int{s.v_bits} {'symmetric block' if s.fmt == 'sym32' else 'affine'} codes") + ")",
         "config": {"workload": s.name, "batch": s.batch, "n_q_heads": s.n_q_heads,
                    "n_kv_heads": s.n_kv_heads, "d_head": s.d_head, "seq_len": s.seq_len,
                    "min_len": s.min_len, "k_bits": s.k_bits, "v_bits": s.v_bits,
                    "k_axis": s.k_axis, "k_group": s.k_group, "k_residual": s.k_residual,
-                   "k_sparse": s.k_sparse, "layers": nlay, "cache_replicas": nrep},
+                   "k_sparse": s.k_sparse, "format": s.fmt, "layers": nlay, "cache_replicas": nrep},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_GBS, "traffic": recorded_traffic(s.cid),
+                     "frac": achieved / PEAK_GBS, "traffic": recorded_traffic(key),
                      "kernel": "kvq_decode_attention (attention kernel + partial merge)",
                      "avg_launch_us": attn_avg_s * 1e6,
                      "p10_p90_us": [float(np.percentile(attn_ms, 10)) * 1e3,
@@ -364,6 +388,9 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=4)
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 1 GiB device copy (HBM reference and counter calibration)")
+    ap.add_argument("--formats", action="store_true",
+                    help="compare the element formats (affine int8, fp8, symmetric blocks at 8 "
+                         "and 4 bits) on the 8-bit per-token workload's shape, one layer")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
@@ -380,14 +407,19 @@ def main():
         copy_probe()
         return
     torch.cuda.set_device(0)
-    cids = [args.config] if args.config else list(DEFAULT_WORKLOADS)
+    if args.formats:
+        runs = format_specs()
+        args.no_cpu_baseline = True
+    else:
+        runs = [(c, None) for c in ([args.config] if args.config else list(DEFAULT_WORKLOADS))]
     results = []
-    for cid in cids:
-        results.append(run_workload(cid, args))
+    for key, spec in runs:
+        results.append(run_workload(key, args, spec))
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-    head = results[-1]
-    s = W.spec(cids[-1])
+    # headline: the largest workload (the affine int8 one in the format comparison)
+    head = results[0] if args.formats else results[-1]
+    s = W.spec(runs[-1][0]) if not args.formats else runs[0][1]
     res = {
         "metric": METRIC,
         "value": head["value"],
@@ -404,8 +436,8 @@ def main():
         "config": head["config"],
         "roofline": head["roofline"],
         "append": head["append"],
-        "workloads": [{k: r[k] for k in ("workload", "value", "unit", "ms_per_step", "roofline", "append")}
-                      for r in results],
+        "workloads": [{k: r[k] for k in ("workload", "value", "unit", "ms_per_step", "dtype", "roofline",
+                                         "append")} for r in results],
     }
     if not args.no_cpu_baseline:
         progress("timing the oracle on the host")

@@ -441,7 +441,6 @@ __device__ __forceinline__ int units_of(const CacheView& c, int L) {
   const int Q = quant_len(c, L);
   return Q > 0 ? (Q + kBlock - 1) / kBlock : (L > 0 ? 1 : 0);
 }
-__device__ __forceinline__ int seq_tiles(const CacheView& c, int b) { return units_of(c, seq_len_of(c, b)); }
 
 // Workgroup whose range holds unit u.
 __device__ __forceinline__ int wg_of_unit(int u, int64_t U, int nwg) {
@@ -451,19 +450,23 @@ __device__ __forceinline__ int wg_of_unit(int u, int64_t U, int nwg) {
 struct UnitPos {
   int b;     // sequence holding the unit (B if the unit is past the last one)
   int base;  // its first unit
+  int len;   // its length (clamped), 0 past the last sequence
 };
 
 // The sequence holding unit u: a wavefront-wide scan of the sequences' unit
 // counts, 256 sequences (4 per lane) at a time. Every lane returns the same.
+// Lengths are loaded at a clamped index, unconditionally, so that the four
+// loads of a lane are in flight together.
 __device__ UnitPos locate_unit(const CacheView& c, int u) {
   const int lane = threadIdx.x & 63;
   int acc = 0;
   for (int cb = 0; cb < c.B; cb += 256) {
-    int n[4], sum = 0;
+    int n[4], len[4], sum = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) len[r] = seq_len_of(c, min(cb + 4 * lane + r, c.B - 1));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int bb = cb + 4 * lane + r;
-      n[r] = bb < c.B ? c.H * seq_tiles(c, bb) : 0;
+      n[r] = cb + 4 * lane + r < c.B ? c.H * units_of(c, len[r]) : 0;
       sum += n[r];
     }
     int incl = sum;  // inclusive scan over the lanes
@@ -481,13 +484,14 @@ __device__ UnitPos locate_unit(const CacheView& c, int u) {
       for (int r = 0; r < 4; ++r) {
         const int nr = __shfl(n[r], ll, 64);
         if (u < base + nr) return UnitPos{__builtin_amdgcn_readfirstlane(cb + 4 * ll + r),
-                                          __builtin_amdgcn_readfirstlane(base)};
+                                          __builtin_amdgcn_readfirstlane(base),
+                                          __builtin_amdgcn_readfirstlane(__shfl(len[r], ll, 64))};
         base += nr;
       }
     }
     acc += chunk;
   }
-  return UnitPos{c.B, __builtin_amdgcn_readfirstlane(acc)};
+  return UnitPos{c.B, __builtin_amdgcn_readfirstlane(acc), 0};
 }
 
 // Units of the sequences before b (a wavefront-wide sum; every lane returns it).
@@ -495,12 +499,12 @@ __device__ int units_before(const CacheView& c, int b) {
   const int lane = threadIdx.x & 63;
   int sum = 0;
   for (int b0 = 0; b0 < b; b0 += 256) {
+    int len[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) len[k] = seq_len_of(c, min(b0 + lane + 64 * k, b - 1));  // in flight together
     int n[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {  // four loads in flight per lane
-      const int bb = b0 + lane + 64 * k;
-      n[k] = bb < b ? seq_tiles(c, bb) : 0;
-    }
+    for (int k = 0; k < 4; ++k) n[k] = b0 + lane + 64 * k < b ? units_of(c, len[k]) : 0;
     sum += c.H * (n[0] + n[1] + n[2] + n[3]);
   }
 #pragma unroll
@@ -582,11 +586,10 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   const int u1 = (int)(((int64_t)iwg + 1) * U / nwg);
   int u = (int)((int64_t)iwg * U / nwg);
   const UnitPos pos = locate_unit(c, u);
-  int b = pos.b, base = pos.base;
+  int b = pos.b, base = pos.base, L = pos.len;
   bool first_seg = true;
   while (u < u1 && b < c.B) {
     // ---- the segment: tiles [k0, k1) of (sequence b, KV head h) -------------
-    const int L = seq_len_of(c, b);
     const int Q = quant_len(c, L);
     const int nt = units_of(c, L);  // > 0: sequences without units are skipped
     const int rel = u - base;
@@ -1134,29 +1137,32 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     // ---- next segment -------------------------------------------------------
     first_seg = false;
     u += k1 - k0;
-    if (k1 == nt && h == c.H - 1) {
+    if (k1 == nt && h == c.H - 1) {  // on to the next sequence with units (L > 0)
       base += c.H * nt;
-      ++b;
-      while (b < c.B && seq_tiles(c, b) == 0) ++b;
+      for (++b; b < c.B; ++b) {
+        L = seq_len_of(c, b);
+        if (L > 0) break;
+      }
     }
   }
 }
 
-// Merge kernel: one workgroup of 128 threads (one per channel) per
-// (sequence, query head) whose output the attention kernel did not write:
-// sequences with no tokens (output 0) and pairs whose units span several
-// workgroups, whose partial results it merges with a log-sum-exp. The
-// partials' (m, l) are staged in LDS by one parallel load; their outputs are
-// loaded 8 at a time.
-__global__ __launch_bounds__(128) void combine_kernel(CacheView c, AttnPlan p, const float* __restrict__ ws,
+// Merge kernel: one workgroup of 256 threads per (sequence, query head)
+// whose output the attention kernel did not write: sequences with no tokens
+// (output 0) and pairs whose units span several workgroups, whose partial
+// results it merges with a log-sum-exp. Thread t takes channel t mod 128 and
+// every second partial (t / 128 says which): it loads kChunk partials' (m, l,
+// o[channel]) at once, so one round trip to memory covers 2 kChunk partials,
+// merges them in registers, and the two halves meet in LDS.
+__global__ __launch_bounds__(256) void combine_kernel(CacheView c, AttnPlan p, const float* __restrict__ ws,
                                                       float* __restrict__ out) {
-  constexpr int kBatch = 128;  // partials staged at a time
-  __shared__ float pml[kBatch][2];
-  const int bq = blockIdx.x, ch = threadIdx.x;
+  constexpr int kChunk = 32;
+  __shared__ float other[3][kD];  // the second half's (M, l, o)
+  const int bq = blockIdx.x, t = threadIdx.x, ch = t & (kD - 1), half = t >> 7;
   const int b = bq / p.Hq, hkv = (bq % p.Hq) / p.group, hh = bq % p.group;
   const int L = seq_len_of(c, b);
   if (L == 0) {
-    out[(size_t)bq * kD + ch] = 0.f;
+    if (half == 0) out[(size_t)bq * kD + ch] = 0.f;
     return;
   }
   const int nt = units_of(c, L);
@@ -1168,43 +1174,56 @@ __global__ __launch_bounds__(128) void combine_kernel(CacheView c, AttnPlan p, c
   // first one, where it is the last segment unless it starts the range
   const bool mid_start = s0 != (int)((int64_t)first * p.units / p.n_wg);
   auto rec = [&](int j) -> const float* {
-    const int wg = first + j;
-    const int slot = 2 * wg + ((j == 0 && mid_start) ? 1 : 0);
+    const int slot = 2 * (first + j) + ((j == 0 && mid_start) ? 1 : 0);
     return ws + ((size_t)slot * p.group + hh) * kPartialFloats;
   };
   float M = -INFINITY, o = 0.f, l = 0.f;
-  for (int j0 = 0; j0 < np; j0 += kBatch) {
-    const int n = min(kBatch, np - j0);
-    __syncthreads();
-    if (ch < n) {
-      const float* pt = rec(j0 + ch);
-      pml[ch][0] = pt[0];
-      pml[ch][1] = pt[1];
+  for (int j0 = half; j0 < np; j0 += 2 * kChunk) {
+    float mv[kChunk], lv[kChunk], ov[kChunk];
+    // loads of a clamped index, unconditional, so that all of them are in
+    // flight together; entries past the last partial are masked afterwards
+#pragma unroll
+    for (int y = 0; y < kChunk; ++y) {
+      const float* pt = rec(min(j0 + 2 * y, np - 1));
+      mv[y] = pt[0];
+      lv[y] = pt[1];
+      ov[y] = pt[4 + ch];
     }
-    __syncthreads();
-    float mb = -INFINITY;
-    for (int j = 0; j < n; ++j) mb = fmaxf(mb, pml[j][0]);
+#pragma unroll
+    for (int y = 0; y < kChunk; ++y)
+      if (j0 + 2 * y >= np) mv[y] = -INFINITY;
+    float mb = mv[0];
+#pragma unroll
+    for (int y = 1; y < kChunk; ++y) mb = fmaxf(mb, mv[y]);
     const float m_new = fmaxf(M, mb);
     if (m_new == -INFINITY) continue;
     const float fo = __builtin_amdgcn_exp2f(M - m_new);
     o *= fo;
     l *= fo;
-    for (int j = 0; j < n; j += 8) {
-      float ov[8];
 #pragma unroll
-      for (int y = 0; y < 8; ++y) ov[y] = (j + y < n) ? rec(j0 + j + y)[4 + ch] : 0.f;
-#pragma unroll
-      for (int y = 0; y < 8; ++y) {
-        if (j + y < n) {
-          const float f = __builtin_amdgcn_exp2f(pml[j + y][0] - m_new);
-          o = __builtin_fmaf(f, ov[y], o);
-          l = __builtin_fmaf(f, pml[j + y][1], l);
-        }
-      }
+    for (int y = 0; y < kChunk; ++y) {  // an absent or empty partial weighs exp2(-inf) = 0
+      const float f = __builtin_amdgcn_exp2f(mv[y] - m_new);
+      o = __builtin_fmaf(f, ov[y], o);
+      l = __builtin_fmaf(f, lv[y], l);
     }
     M = m_new;
   }
-  out[(size_t)bq * kD + ch] = (l > 0.f) ? o / l : 0.f;
+  if (half == 1) {
+    other[0][ch] = M;
+    other[1][ch] = l;
+    other[2][ch] = o;
+  }
+  __syncthreads();
+  if (half == 0) {
+    const float M2 = other[0][ch], m_new = fmaxf(M, M2);
+    float lt = 0.f, ot = 0.f;
+    if (m_new != -INFINITY) {
+      const float f1 = __builtin_amdgcn_exp2f(M - m_new), f2 = __builtin_amdgcn_exp2f(M2 - m_new);
+      lt = f1 * l + f2 * other[1][ch];
+      ot = f1 * o + f2 * other[2][ch];
+    }
+    out[(size_t)bq * kD + ch] = (lt > 0.f) ? ot / lt : 0.f;
+  }
 }
 
 // Launch of one kernel variant, or (occ != nullptr) its resident workgroups
@@ -1303,7 +1322,7 @@ hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p, const 
     if (e != hipSuccess) return e;
   }
   if (!p.need_combine) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(c.B * p.Hq), dim3(kD), 0, st, c, p, ws, out);
+  hipLaunchKernelGGL(combine_kernel, dim3(c.B * p.Hq), dim3(256), 0, st, c, p, ws, out);
   return hipGetLastError();
 }
 

@@ -33,6 +33,15 @@ def test_algorithmic_bytes_match_oracle_sizes_on_full_caches(cid):
     assert bench.algorithmic_bytes(s, [T] * s.batch) == cache + q_out
 
 
+@pytest.mark.parametrize("fmt,kb,vb", [("fp8", 8, 8), ("sym32", 8, 8), ("sym32", 4, 2)])
+def test_algorithmic_bytes_of_element_formats(fmt, kb, vb):
+    s = replace(W.spec(3), batch=2, fmt=fmt, k_bits=kb, v_bits=vb)
+    T = 256
+    sz = actual_bytes(ref_config(s), s.batch, T)
+    cache = sz["k_codes"] + sz["k_meta"] + sz["v_codes"] + sz["v_meta"]
+    assert bench.algorithmic_bytes(s, [T] * s.batch) == cache + s.batch * s.n_q_heads * s.d_head * 6
+
+
 def test_algorithmic_bytes_count_residual_keys_as_fp16():
     s = replace(W.spec(2), batch=1)
     D, H = s.d_head, s.n_kv_heads
@@ -167,3 +176,23 @@ def test_bench_main_with_gpu_calls_stubbed(argv, monkeypatch, capsys):
     if "cpu_baseline" in d:
         assert d["cpu_baseline"]["kind"] == "oracle" and d["cpu_baseline"]["value"] > 0
     assert len(d["workloads"]) == 1 and d["workloads"][0]["value"] == d["value"]
+
+
+def test_bench_formats_mode(monkeypatch, capsys):
+    """--formats runs the 8-bit per-token shape in the four element formats
+    (shrunk here) and reports each one's bytes and roofline."""
+    import json
+    _stub_gpu(monkeypatch)
+    monkeypatch.setattr(W, "SPECS", {**W.SPECS, 3: replace(W.SPECS[3], seq_len=640, min_len=640)})
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--formats", "--steps", "2", "--warmup", "1",
+                                      "--settle-ms", "0"])
+    bench.main()
+    d = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    ws = d["workloads"]
+    assert len(ws) == 4 and "cpu_baseline" not in d
+    assert d["roofline"] == ws[0]["roofline"]
+    # bytes per (token, KV head): int8 128+4+128+4, fp8 128+128, 8-bit blocks
+    # 128+8+128+8, 4-bit blocks 64+8+64+8
+    b = [w["roofline"]["algorithmic_bytes_per_launch"] for w in ws]
+    assert b[1] < b[0] < b[2] and b[3] < b[1]
+    assert "fp8" in ws[1]["dtype"] and "symmetric" in ws[3]["dtype"]
