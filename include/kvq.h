@@ -210,8 +210,9 @@ typedef struct kvq_sizes {
 
 /* Fills *out_host. max_tokens must be a positive multiple of 32;
  * KVQ_EINVAL on a bad configuration, size or null pointer, KVQ_EUNSUPPORTED
- * past 2^24 tokens per sequence (the capacity a kvq_cache can describe).
- * Pure host function. */
+ * past 2^24 tokens per sequence (the capacity a kvq_cache can describe) or
+ * past 2^44 (sequence, KV head, token) slots in all (where byte counts would
+ * leave 64-bit range). Pure host function. */
 kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch,
                            int64_t max_tokens, kvq_sizes* out_host);
 

@@ -134,15 +134,44 @@ class KVCache:
     def lengths(self):
         return list(self.len_host)
 
+    _ARRAYS = ("k_codes", "k_meta", "k_resid", "k_sparse", "v_codes", "v_meta", "seq_len")
+
     def copy_from(self, other):
         """Copy the whole state of another cache of the same shape (device
         buffers and host lengths)."""
-        for name in ("k_codes", "k_meta", "k_resid", "k_sparse", "v_codes", "v_meta", "seq_len"):
+        for name in self._ARRAYS:
             a, b = getattr(self, name), getattr(other, name)
             if a is not None:
                 a.copy_(b)
         for i in range(self.batch):
             self.len_host[i] = other.len_host[i]
+
+    def state(self):
+        """Checkpoint: host copies of every device buffer and the lengths (a
+        dict of numpy arrays). Synchronizes with the device."""
+        import numpy as np
+        out = {name: getattr(self, name).cpu().numpy() for name in self._ARRAYS
+               if getattr(self, name) is not None}
+        out["len_host"] = np.array(list(self.len_host), np.int32)
+        return out
+
+    def load_state(self, st):
+        """Resume from state(): every buffer and the lengths are overwritten
+        (same configuration and shape required)."""
+        import torch
+        for name in self._ARRAYS:
+            a = getattr(self, name)
+            if a is None:
+                continue
+            src = st[name]
+            if tuple(src.shape) != tuple(a.shape) or str(src.dtype) != str(a.dtype).replace("torch.", ""):
+                raise ValueError(f"{name}: checkpoint {src.dtype}{tuple(src.shape)} does not fit "
+                                 f"{a.dtype}{tuple(a.shape)}")
+            a.copy_(torch.from_numpy(src))
+        if len(st["len_host"]) != self.batch:
+            raise ValueError("len_host: wrong batch")
+        for i in range(self.batch):
+            self.len_host[i] = int(st["len_host"][i])
 
 
 def kvq_append(cache, k_new, v_new, cu_new, n_new, stream=None):

@@ -143,9 +143,12 @@ kvq_status check_config(const kvq_config* cfg) {
   return KVQ_OK;
 }
 
-kvq_status check_shape(int32_t batch, int64_t max_tokens) {
+// Shape of a cache for a valid cfg. Beyond 2^44 (sequence, KV head, token)
+// slots (4 PB of fp16 keys) the byte counts would leave 64-bit range.
+kvq_status check_shape(const kvq_config* cfg, int32_t batch, int64_t max_tokens) {
   if (batch < 1 || max_tokens < kBlock || max_tokens % kBlock != 0) return KVQ_EINVAL;
   if (max_tokens > (1 << 24)) return KVQ_EUNSUPPORTED;
+  if ((int64_t)batch * cfg->n_kv_heads > ((int64_t)1 << 44) / max_tokens) return KVQ_EUNSUPPORTED;
   return KVQ_OK;
 }
 
@@ -153,7 +156,7 @@ bool aligned(const void* p) { return ((uintptr_t)p & 255u) == 0; }
 
 kvq_status check_cache(const kvq_config* cfg, const kvq_cache* c) {
   if (!c) return KVQ_EINVAL;
-  kvq_status s = check_shape(c->batch, c->max_tokens);
+  kvq_status s = check_shape(cfg, c->batch, c->max_tokens);
   if (s != KVQ_OK) return s;
   const void* req[] = {c->k_codes, c->v_codes, c->seq_len};
   for (const void* p : req)
@@ -268,7 +271,7 @@ kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch, int64_t max_tok
                            kvq_sizes* out) {
   kvq_status s = check_config(cfg);
   if (s != KVQ_OK) return s;
-  if ((s = check_shape(batch, max_tokens)) != KVQ_OK) return s;
+  if ((s = check_shape(cfg, batch, max_tokens)) != KVQ_OK) return s;
   if (!out) return KVQ_EINVAL;
   const uint64_t n = (uint64_t)batch * cfg->n_kv_heads, T = (uint64_t)max_tokens, D = kD;
   memset(out, 0, sizeof(*out));
@@ -292,7 +295,7 @@ kvq_status kvq_cache_sizes(const kvq_config* cfg, int32_t batch, int64_t max_tok
 }
 
 size_t kvq_workspace_bytes(const kvq_config* cfg, int32_t batch, int64_t max_tokens) {
-  if (check_config(cfg) != KVQ_OK || check_shape(batch, max_tokens) != KVQ_OK) return 0;
+  if (check_config(cfg) != KVQ_OK || check_shape(cfg, batch, max_tokens) != KVQ_OK) return 0;
   return workspace_bytes_for(max_wgs_for(batch, cfg->n_kv_heads, max_tokens), cfg->n_q_heads / cfg->n_kv_heads);
 }
 
