@@ -39,6 +39,10 @@ Modules:
           packed byte layout, dequantized tensors, float64 attention, and the
           log-sum-exp merge of split partials (softmax_partial, merge_partials)
   sizes   the bytes-per-token formula and the actual cache sizes
+  rope    the rotary embedding applied to pre-RoPE cached keys inside
+          attention (KVQuant's pre-RoPE keys, [P1-kivi]); textbook RoPE, since
+          the pages define none: parity unpinned by the pages, pinned by the
+          embedding's own properties
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against values the
 pages print, closed forms, invariants and brute force. One part has no pin in

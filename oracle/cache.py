@@ -31,7 +31,7 @@ include/kvq.h documents.
 """
 import numpy as np
 
-from . import fp8, quant
+from . import fp8, quant, rope
 
 F16 = np.float16
 BLOCK = 32  # tokens per per-channel key group and per value code block
@@ -43,7 +43,7 @@ class Config:
     def __init__(self, d_head=128, n_kv_heads=1, n_q_heads=1, k_bits=8, v_bits=8,
                  k_axis="token", k_group_tokens=0, k_residual_tokens=0,
                  k_sparse_per_vector=0, k_format="int", v_format="int",
-                 k_scale=1.0, v_scale=1.0):
+                 k_scale=1.0, v_scale=1.0, k_rope=0, rope_theta=10000.0):
         self.d_head = d_head
         self.n_kv_heads = n_kv_heads
         self.n_q_heads = n_q_heads
@@ -58,6 +58,8 @@ class Config:
         self.v_format = v_format
         self.k_scale = k_scale            # fp8 only: the per-cache fp32 scales
         self.v_scale = v_scale
+        self.k_rope = k_rope              # 1: keys cached before the rotary embedding,
+        self.rope_theta = rope_theta      # which attention applies (oracle/rope.py)
 
     @property
     def per_channel(self):
@@ -240,7 +242,9 @@ class RefCache:
     # ----------------------------------------------------------- attention
     def attention(self, q16, softmax_scale, pairs=None):
         """Decode attention in float64 ([P2-dec]; the plain definition
-        out = softmax(scale * q . K_hat) V_hat over every held token).
+        out = softmax(scale * q . K_hat) V_hat over every held token; with
+        k_rope, K_hat rotated by each key's position first, the query taken as
+        already rotated).
 
         q16: fp16 [B, Hq, D]. Returns float64 [B, Hq, D]. Query head h reads
         KV head h // (Hq/H). pairs: optional iterable of (b, kv_head) to
@@ -255,6 +259,8 @@ class RefCache:
             if self.length[b] == 0:
                 continue
             K = self.k_hat(b, h)
+            if self.cfg.k_rope:           # pre-RoPE keys: rotate by position after dequantization
+                K = rope.rope(K, np.arange(K.shape[0]), self.cfg.rope_theta)
             V = self.v_hat(b, h)
             for hq in range(h * grp, (h + 1) * grp):
                 qv = q16[b, hq].astype(np.float64)
