@@ -196,7 +196,9 @@ def format_specs():
     """The 8-bit per-token workload's shape (B=1, Hq=32, Hkv=8, S=32768), one
     layer, in each element format: affine int8 (the workload's own), fp8 E4M3
     with per-cache scales, and symmetric 32-channel blocks at 8 and 4 bits
-    (llama.cpp's q8_0 / q4_0 block shapes)."""
+    (llama.cpp's q8_0 / q4_0 block shapes); then the int4 KIVI workload with
+    its keys cached before the rotary embedding (rotated inside attention),
+    to compare with the default run's plain one."""
     from dataclasses import replace
     from quantized_decode_attention_03_amd import workloads as W
     base = W.spec(3, layers=1)
@@ -207,6 +209,8 @@ def format_specs():
         ("3-sym8", replace(base, fmt="sym32", name=f"int8 symmetric 32-channel blocks K/V, {shape}")),
         ("3-sym4", replace(base, fmt="sym32", k_bits=4, v_bits=4,
                            name=f"int4 symmetric 32-channel blocks K/V, {shape}")),
+        # the int4 KIVI workload with keys cached before the rotary embedding
+        ("2-rope", replace(W.spec(2), k_rope=1, name=W.spec(2).name + ", keys pre-RoPE")),
     ]
 
 
@@ -361,7 +365,8 @@ def run_workload(key, args, s=None):
                    "n_kv_heads": s.n_kv_heads, "d_head": s.d_head, "seq_len": s.seq_len,
                    "min_len": s.min_len, "k_bits": s.k_bits, "v_bits": s.v_bits,
                    "k_axis": s.k_axis, "k_group": s.k_group, "k_residual": s.k_residual,
-                   "k_sparse": s.k_sparse, "format": s.fmt, "layers": nlay, "cache_replicas": nrep},
+                   "k_sparse": s.k_sparse, "format": s.fmt, "k_rope": s.k_rope, "layers": nlay,
+                   "cache_replicas": nrep},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBS, "traffic": recorded_traffic(key),
                      "kernel": "kvq_decode_attention (attention kernel + partial merge)",
@@ -390,7 +395,8 @@ def main():
                     help="time a plain 1 GiB device copy (HBM reference and counter calibration)")
     ap.add_argument("--formats", action="store_true",
                     help="compare the element formats (affine int8, fp8, symmetric blocks at 8 "
-                         "and 4 bits) on the 8-bit per-token workload's shape, one layer")
+                         "and 4 bits) on the 8-bit per-token workload's shape, one layer, and "
+                         "pre-RoPE keys on the int4 KIVI workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "

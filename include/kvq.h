@@ -47,6 +47,19 @@
  *                         stored u_i = q_i - q_min, x_hat_i = s * q_i.
  *     Both formats keep keys on the token axis and apply to keys and values
  *     alike (k_format == v_format).
+ *   - Pre-RoPE keys (k_rope = 1): keys are quantized before the rotary
+ *     position embedding and attention rotates each dequantized key by its
+ *     position, so the rotation does not smear the channel structure the
+ *     per-channel scales rely on (KVQuant, as described in "Sub-8-Bit KV
+ *     Cache Quantization ...", "What the low-bit numbers actually cost"). The
+ *     pages define no embedding; this is the textbook one:
+ *       theta_i = rope_theta^(-2 i / D), i = 0 .. D/2 - 1, and key t (0-based
+ *       position in its sequence) becomes, for each pair (i, i + D/2),
+ *         y_i       = x_i cos(t theta_i) - x_{i+D/2} sin(t theta_i)
+ *         y_{i+D/2} = x_{i+D/2} cos(t theta_i) + x_i sin(t theta_i);
+ *     the query passed to attention is already rotated by its own position.
+ *     Channel-axis affine keys without sparse entries only. kvq_dequantize
+ *     returns the keys as cached (before the rotation).
  *
  * Exact arithmetic of one quantization group (x_i are fp16 values widened to
  * fp32; every operation is IEEE fp32 with round-to-nearest-even):
@@ -181,6 +194,10 @@ typedef struct kvq_config {
   int32_t v_format;            /* equal to k_format                          */
   float k_scale;               /* FP8 only: per-cache key scale, finite > 0  */
   float v_scale;               /* FP8 only: per-cache value scale            */
+  int32_t k_rope;              /* 1: keys are cached before the rotary
+                                  embedding, which attention applies; 0: keys
+                                  are used as cached                         */
+  float rope_theta;            /* k_rope only: frequency base (> 1, finite)  */
 } kvq_config;
 
 /* Host-side descriptor of one cache; pointers name device memory except

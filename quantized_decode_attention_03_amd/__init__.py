@@ -26,7 +26,8 @@ class Config:
 
     def __init__(self, n_kv_heads, n_q_heads, k_bits, v_bits, k_axis="token",
                  k_group_tokens=0, k_residual_tokens=0, k_sparse_per_vector=0, d_head=128,
-                 k_format="int", v_format=None, k_scale=1.0, v_scale=1.0):
+                 k_format="int", v_format=None, k_scale=1.0, v_scale=1.0, k_rope=0,
+                 rope_theta=10000.0):
         self.d_head = d_head
         self.n_kv_heads = n_kv_heads
         self.n_q_heads = n_q_heads
@@ -43,11 +44,14 @@ class Config:
                 raise ValueError(f"format {f!r}: expected one of {sorted(_FORMATS)}")
         self.k_scale = k_scale
         self.v_scale = v_scale
+        self.k_rope = k_rope          # 1: keys cached before the rotary embedding
+        self.rope_theta = rope_theta
 
     @classmethod
     def from_spec(cls, s):
         return cls(s.n_kv_heads, s.n_q_heads, s.k_bits, s.v_bits, s.k_axis, s.k_group,
-                   s.k_residual, s.k_sparse, s.d_head, s.fmt, s.fmt, s.k_scale, s.v_scale)
+                   s.k_residual, s.k_sparse, s.d_head, s.fmt, s.fmt, s.k_scale, s.v_scale,
+                   s.k_rope, s.rope_theta)
 
     def c(self):
         return N.kvq_config(self.d_head, self.n_kv_heads, self.n_q_heads, self.k_bits,
@@ -55,7 +59,8 @@ class Config:
                             N.KVQ_AXIS_CHANNEL if self.k_axis == "channel" else N.KVQ_AXIS_TOKEN,
                             self.k_group_tokens, self.k_residual_tokens, self.d_head,
                             self.k_sparse_per_vector, _FORMATS[self.k_format],
-                            _FORMATS[self.v_format], self.k_scale, self.v_scale)
+                            _FORMATS[self.v_format], self.k_scale, self.v_scale, self.k_rope,
+                            self.rope_theta)
 
 
 def _ptr(t):

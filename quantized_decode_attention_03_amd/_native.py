@@ -23,7 +23,8 @@ class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_head", "n_kv_heads", "n_q_heads", "k_bits", "v_bits", "k_axis", "k_group_tokens",
         "k_residual_tokens", "v_group_channels", "k_sparse_per_vector", "k_format",
-        "v_format")] + [("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+        "v_format")] + [("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                        ("k_rope", ctypes.c_int32), ("rope_theta", ctypes.c_float)]
 
 
 class kvq_cache(ctypes.Structure):

@@ -130,6 +130,12 @@ kvq_status check_config(const kvq_config* cfg) {
     for (float sc : {cfg->k_scale, cfg->v_scale})
       if (!(sc > 0.0f) || !std::isfinite(sc)) return KVQ_EINVAL;
   }
+  if (cfg->k_rope != 0 && cfg->k_rope != 1) return KVQ_EINVAL;
+  if (cfg->k_rope) {
+    if (!(cfg->rope_theta > 1.0f) || !std::isfinite(cfg->rope_theta)) return KVQ_EINVAL;
+    if (cfg->k_axis != KVQ_AXIS_CHANNEL || fmt != KVQ_FORMAT_INT || cfg->k_sparse_per_vector != 0)
+      return KVQ_EUNSUPPORTED;
+  }
   if (cfg->k_axis == KVQ_AXIS_TOKEN) {
     if (cfg->k_group_tokens != 0 || cfg->k_residual_tokens != 0) return KVQ_EINVAL;
     if (cfg->k_sparse_per_vector != 0) return KVQ_EUNSUPPORTED;
@@ -216,7 +222,9 @@ kvq_status decode_attention(const kvq_config* cfg, const kvq_cache* cache, const
   p.Hq = cfg->n_q_heads;
   p.group = cfg->n_q_heads / cfg->n_kv_heads;
   p.scale = softmax_scale;
-  plan_attention(cfg, cache, (int64_t)compute_units() * attention_blocks_per_cu(v, p.group), &p);
+  p.rope = cfg->k_rope;
+  p.rope_log2_theta = cfg->k_rope ? (double)log2l((long double)cfg->rope_theta) : 0.0;
+  plan_attention(cfg, cache, (int64_t)compute_units() * attention_blocks_per_cu(v, p.group, p.rope), &p);
   if (own_scratch) {
     if (workspace_bytes_for(p.n_wg, p.group) > ws_bytes) return KVQ_EWORKSPACE;
     if (!ws) return KVQ_EHIP;

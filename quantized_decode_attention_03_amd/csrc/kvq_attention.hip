@@ -295,6 +295,37 @@ __device__ __forceinline__ Frag sym_key_frag(uint32_t w0, uint32_t w1) {
   return f;
 }
 
+// Rotary-embedding keys: MFMA j of lane group g takes channels [16 g, 16 g +
+// 16) (j = 0, 1) and their rotation partners, 64 higher (j = 2, 3), in the
+// in-chunk order of the affine layout, so every lane holds both channels of
+// each of its pairs and chunk j + 2 pairs up with chunk j element by element.
+template <int KB>
+__device__ __forceinline__ int rope_channel(int grp, int j, int p, int s) {
+  return ((j >> 1) ? 64 : 0) + 16 * grp + key_channel<KB>(0, j & 1, p, s);
+}
+
+// cos and sin of the rotation angle t theta_i, from the angle in revolutions
+// t phi_i = t theta_i / (2 pi) (phi_i = ph.x + ph.y, two floats): the product
+// t * ph.x is split into its rounded value and exact error (t < 2^24 is exact
+// in fp32), the whole revolutions are dropped, and what is left, in [-1/2,
+// 1/2] to about 2^-25, goes to the hardware sine and cosine, which take
+// revolutions.
+__device__ __forceinline__ void rope_cs(float t, float2 ph, float& c, float& s) {
+#pragma clang fp contract(off)
+  const float p = t * ph.x;
+  const float e = __builtin_fmaf(t, ph.x, -p);
+  const float r = (p - __builtin_rintf(p)) + __builtin_fmaf(t, ph.y, e);
+  c = __builtin_amdgcn_cosf(r);
+  s = __builtin_amdgcn_sinf(r);
+}
+
+// fp16 hi and lo parts of two floats (y - hi is exact): the A operands of two
+// products whose sum keeps about 22 bits of y.
+__device__ __forceinline__ void split_hilo(float y0, float y1, uint32_t& hi, uint32_t& lo) {
+  hi = pk_rtz(y0, y1);
+  lo = pk_rtz(y0 - f16lo(hi), y1 - f16hi(hi));
+}
+
 // Geometry of one 32-token tile as staged in LDS:
 //   [key codes 32 x 16*KB][value block 128 x 4*VB][value meta, 32 tokens]
 //   [key meta: 128 words (channel axis) or 32 tokens (token axis)]
@@ -318,7 +349,7 @@ struct Geom {
   static constexpr int kBytes = kK + kV + kVm + kKm + kSp;
   static constexpr int kLoads = kK / 1024 + kV / 1024 + kMetaLoads;  // DMA instructions per tile
   // the key-product B operand and zero-point operand (channel axis only)
-  static constexpr int kWaveLds = KAXIS ? (4 * (2 * G) * 4 * 16 + 4 * 4 * 4 * 4) : 0;
+  static constexpr int kWaveLds = (KAXIS && FMT != kFmtRope) ? (4 * (2 * G) * 4 * 16 + 4 * 4 * 4 * 4) : 0;
   // tile slots per wavefront: as many as fit the per-wavefront budget, 2 to 6
   static constexpr int kSlotsFit = (kWaveBudget - kWaveLds - (SPARSE ? G * kD : 0)) / kBytes;
   static constexpr int kSlots = kSlotsFit < 2 ? 2 : (kSlotsFit > 6 ? 6 : kSlotsFit);
@@ -516,8 +547,9 @@ template <int KB, int VB, int KAXIS, int G, bool SPARSE, int FMT>
 __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, const uint16_t* __restrict__ q,
                                                    float* __restrict__ out, float* __restrict__ ws) {
   using Gm = Geom<KB, VB, KAXIS, G, SPARSE, FMT>;
-  constexpr bool kFp8 = FMT == kFmtFp8, kSym = FMT == kFmtSym32;
-  static_assert(FMT == kFmtInt || (KAXIS == 0 && !SPARSE), "fp8 and block formats are token-axis only");
+  constexpr bool kFp8 = FMT == kFmtFp8, kSym = FMT == kFmtSym32, kRope = FMT == kFmtRope;
+  static_assert(FMT == kFmtInt || kRope || (KAXIS == 0 && !SPARSE), "fp8 and block formats are token-axis only");
+  static_assert(!kRope || (KAXIS == 1 && !SPARSE), "rotary keys: channel axis, no sparse entries");
   static_assert(!kFp8 || (KB == 8 && VB == 8), "fp8 codes are bytes");
   constexpr int NB = Gm::kSlots;
   constexpr int kQMinK = -(1 << (KB - 1));
@@ -557,6 +589,17 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMain > kMerge ? kMain : kMerge];
   // query heads pre-scaled for the sparse entries (written identically by every wavefront)
   __shared__ float qsh[SPARSE ? G : 1][SPARSE ? kD : 1];
+  // rotary keys: revolutions per token of frequency i, theta_i / (2 pi) with
+  // theta_i = base^(-i / 64), as two floats (computed in double)
+  __shared__ float2 rphi[kRope ? 64 : 1];
+  if constexpr (kRope) {
+    if (tid < 64) {
+      const double ph = exp2(-(double)tid / 64.0 * p.rope_log2_theta) * 0.15915494309189533577;
+      const float hi = (float)ph;
+      rphi[tid] = make_float2(hi, (float)(ph - (double)hi));
+    }
+    __syncthreads();
+  }
 
   uint8_t* wbase = smem + w * kWaveBytes;             // this wavefront's slots
   WaveLds<G>& wl = *reinterpret_cast<WaveLds<G>*>(wbase + NB * Gm::kBytes);
@@ -678,9 +721,9 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     // token axis: the B operand is the raw fp16 query of head n mod G (exact);
     // qsum_u = unit * sum_c q_c for the zero-point term (symmetric blocks: the
     // sum over each block's channels, qsum_b[j])
-    Frag qfrag[KAXIS ? 1 : 4];
+    Frag qfrag[(KAXIS && !kRope) ? 1 : 4];
     float qsum_u = 0.f, qsum_b[kSym ? kSymBlocks : 1];
-    if constexpr (KAXIS) {
+    if constexpr (KAXIS && !kRope) {
       const float qs = qscale * (float)(1 << (kShK - bsh));
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
@@ -696,8 +739,11 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
         for (int pp = 0; pp < 4; ++pp) {
           // symmetric blocks: MFMA j covers channel block j (lane group and
           // chunk roles swapped)
-          const int ch0 = kSym ? key_channel<KB>(j, grp, pp, 0) : key_channel<KB>(grp, j, pp, 0);
-          const int ch1 = kSym ? key_channel<KB>(j, grp, pp, 1) : key_channel<KB>(grp, j, pp, 1);
+          // (rotary keys: a chunk and its partner chunk hold each pair's channels)
+          const int ch0 = kRope ? rope_channel<KB>(grp, j, pp, 0)
+                                : (kSym ? key_channel<KB>(j, grp, pp, 0) : key_channel<KB>(grp, j, pp, 0));
+          const int ch1 = kRope ? rope_channel<KB>(grp, j, pp, 1)
+                                : (kSym ? key_channel<KB>(j, grp, pp, 1) : key_channel<KB>(grp, j, pp, 1));
           const uint32_t a0 = qlds[hq * kD + ch0], a1 = qlds[hq * kD + ch1];
           qfrag[j].p[pp] = a0 | (a1 << 16);
           sj += h2f((uint16_t)a0) + h2f((uint16_t)a1);
@@ -887,7 +933,23 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const uint8_t* rowb = kbuf + a_token(e, c16) * Gm::kRowK;
-        if constexpr (kSym) {
+        if constexpr (kRope) {
+          // channels [16 grp, +16) (2 KB bytes at 2 KB grp) and their partners
+          // 64 higher (8 KB bytes on): KB / 2 words each
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const uint8_t* src = rowb + hf * 8 * KB + 2 * KB * grp;
+            if constexpr (KB == 8) {
+              const uint4 y = reinterpret_cast<const uint4*>(src)[0];
+              kc[e][4 * hf] = y.x; kc[e][4 * hf + 1] = y.y; kc[e][4 * hf + 2] = y.z; kc[e][4 * hf + 3] = y.w;
+            } else if constexpr (KB == 4) {
+              const uint2 y = reinterpret_cast<const uint2*>(src)[0];
+              kc[e][2 * hf] = y.x; kc[e][2 * hf + 1] = y.y;
+            } else {
+              kc[e][hf] = reinterpret_cast<const uint32_t*>(src)[0];
+            }
+          }
+        } else if constexpr (kSym) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             if constexpr (KB == 8) {
@@ -912,7 +974,62 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
       }
       float sc[8];
       float cs;
-      if constexpr (KAXIS) {
+      if constexpr (kRope) {
+        // keys dequantized exactly, x = s (u - z) + s q_min, rotated by their
+        // positions and split into fp16 hi and lo parts: two products each
+        // with the raw query; chunk jj and its partner chunk jj + 2
+        f4v s[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
+        const float tq[2] = {(float)(t0 + a_token(0, c16)), (float)(t0 + a_token(1, c16))};
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          Frag fa[2], fb[2], ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            fa[e] = key_frag<KB, true>(kc[e], jj);
+            fb[e] = key_frag<KB, true>(kc[e], jj + 2);
+          }
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            float ya[2][2], yb[2][2];  // [row block][half]
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs) {
+              const int cc = 16 * grp + key_channel<KB>(0, jj, pp, hs);  // frequency index
+              const uint32_t ma = kmeta[cc], mb = kmeta[cc + 64];
+              // x = operand * (s / unit) + s (q_min - z), exact in fp32
+              const float sa = f16lo(ma), sb = f16lo(mb);
+              const float aa = sa * kInvUnitK, ab = sb * kInvUnitK;
+              const float ba = sa * ((float)kQMinK - f16hi(ma)), bb = sb * ((float)kQMinK - f16hi(mb));
+              const float2 ph = rphi[cc];
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const float xa = __builtin_fmaf(hs ? f16hi(fa[e].p[pp]) : f16lo(fa[e].p[pp]), aa, ba);
+                const float xb = __builtin_fmaf(hs ? f16hi(fb[e].p[pp]) : f16lo(fb[e].p[pp]), ab, bb);
+                float cr, sr;
+                rope_cs(tq[e], ph, cr, sr);
+                ya[e][hs] = __builtin_fmaf(xa, cr, -xb * sr);
+                yb[e][hs] = __builtin_fmaf(xb, cr, xa * sr);
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              split_hilo(ya[e][0], ya[e][1], ah[e].p[pp], al[e].p[pp]);
+              split_hilo(yb[e][0], yb[e][1], bh[e].p[pp], bl[e].p[pp]);
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            s[e] = mfma(ah[e], qfrag[jj], s[e]);
+            s[e] = mfma(al[e], qfrag[jj], s[e]);
+            s[e] = mfma(bh[e], qfrag[jj + 2], s[e]);
+            s[e] = mfma(bl[e], qfrag[jj + 2], s[e]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[4 * e + r] = s[e][r];
+        cs = qscale;
+      } else if constexpr (KAXIS) {
         build_qb(kmeta[bc0], kmeta[bc1], true);
         // zero-point term, the same for every token of the block
         f4v cz = {0.f, 0.f, 0.f, 0.f};
@@ -1031,8 +1148,8 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           dma16(rv, (uint32_t)(t0 / kBlock) * Gm::kV + x * 1024 + lane * 16, lv + x * 1024);
         if (lane < 8) dma16(rvm, (uint32_t)t0 * 4 + lane * 16, lm);
         // B operand: query scaled by the softmax factor only (the pair's 2^lf
-        // cancelled), hi/lo
-        build_qb(kres, kres, false);
+        // cancelled), hi/lo; rotary keys use the raw query operand instead
+        if constexpr (!kRope) build_qb(kres, kres, false);
 #pragma nounroll
         for (int e = 0; e < 2; ++e) {
           // keys of row block e: LDS row m (0..15) = token t0 + a_token(e, m);
@@ -1045,16 +1162,46 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           wait_vm<0>();
           uint32_t rk[16];
           {
-            const uint4* kr4 = reinterpret_cast<const uint4*>(kres_lds + c16 * (kD * 2) + grp * 64);
+            // the lane's 32 channels of its row (rotary keys: [16 grp, +16)
+            // and the partners 64 higher)
+            const uint4* kr4 = reinterpret_cast<const uint4*>(kres_lds + c16 * (kD * 2) + (kRope ? 32 : 64) * grp);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-              const uint4 v = kr4[x];
+              const uint4 v = kr4[kRope ? (x & 1) + 8 * (x >> 1) : x];
               rk[4 * x] = v.x; rk[4 * x + 1] = v.y; rk[4 * x + 2] = v.z; rk[4 * x + 3] = v.w;
             }
           }
           f4v s1 = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (kRope) {
+            // rotate by position, split hi / lo, two products with the raw query
+            const float tq = (float)(t0 + a_token(e, c16));
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+            for (int jj = 0; jj < 2; ++jj) {
+              Frag ah, al, bh, bl;
+#pragma unroll
+              for (int pp = 0; pp < 4; ++pp) {
+                float ya[2], yb[2];
+#pragma unroll
+                for (int hs = 0; hs < 2; ++hs) {
+                  const int o = key_channel<KB>(0, jj, pp, hs);  // channel 16 grp + o
+                  const float xa = (o & 1) ? f16hi(rk[o >> 1]) : f16lo(rk[o >> 1]);
+                  const float xb = (o & 1) ? f16hi(rk[8 + (o >> 1)]) : f16lo(rk[8 + (o >> 1)]);
+                  float cr, sr;
+                  rope_cs(tq, rphi[16 * grp + o], cr, sr);
+                  ya[hs] = __builtin_fmaf(xa, cr, -xb * sr);
+                  yb[hs] = __builtin_fmaf(xb, cr, xa * sr);
+                }
+                split_hilo(ya[0], ya[1], ah.p[pp], al.p[pp]);
+                split_hilo(yb[0], yb[1], bh.p[pp], bl.p[pp]);
+              }
+              s1 = mfma(ah, qfrag[jj], s1);
+              s1 = mfma(al, qfrag[jj], s1);
+              s1 = mfma(bh, qfrag[jj + 2], s1);
+              s1 = mfma(bl, qfrag[jj + 2], s1);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < (kRope ? 0 : 4); ++j) {
             // k-slot pair pp of chunk j: the keys of the channels the codes use
             Frag kf;
 #pragma unroll
@@ -1068,7 +1215,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           float sc[8];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {  // tokens 8grp + 4e + r: slots 4e + r
-            const float v = add_ror<G>(s1[r]);
+            const float v = kRope ? s1[r] : add_ror<G>(s1[r]);
             sc[r] = (e == 0) ? v : -INFINITY;
             sc[4 + r] = (e == 0) ? -INFINITY : v;
           }
@@ -1081,7 +1228,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           }
 #pragma unroll
           for (int j = 0; j < 8; ++j) val_words<VB>(vres_lds + (16 * j + c16) * 4 * VB, grp, vcl[j], vch[j]);
-          softmax_pv(sc, 1.f, vm, vcl, vch, t0, L);
+          softmax_pv(sc, kRope ? qscale : 1.f, vm, vcl, vch, t0, L);
           wait_lgkm0();  // the keys are read before the next half's loads
           wave_lds_fence();
         }
@@ -1273,12 +1420,17 @@ hipError_t dispatch_g(const CacheView& c, const AttnPlan& p, const uint16_t* q, 
 template <int KB, int VB, int FMT>
 hipError_t dispatch_axis(const CacheView& c, const AttnPlan& p, const uint16_t* q, float* out, float* ws,
                          hipStream_t st, int* occ) {
-  if (c.kaxis == 0) return dispatch_g<KB, VB, 0, false, FMT>(c, p, q, out, ws, st, occ);
-  if constexpr (FMT == kFmtInt) {
-    if (c.sparse) return dispatch_g<KB, VB, 1, true, FMT>(c, p, q, out, ws, st, occ);
+  if constexpr (FMT == kFmtRope) {  // channel axis, no sparse entries
+    if (c.kaxis != 1 || c.sparse) return hipErrorInvalidValue;
     return dispatch_g<KB, VB, 1, false, FMT>(c, p, q, out, ws, st, occ);
+  } else {
+    if (c.kaxis == 0) return dispatch_g<KB, VB, 0, false, FMT>(c, p, q, out, ws, st, occ);
+    if constexpr (FMT == kFmtInt) {
+      if (c.sparse) return dispatch_g<KB, VB, 1, true, FMT>(c, p, q, out, ws, st, occ);
+      return dispatch_g<KB, VB, 1, false, FMT>(c, p, q, out, ws, st, occ);
+    }
+    return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
 }
 
 template <int KB, int FMT>
@@ -1310,6 +1462,7 @@ hipError_t dispatch(const CacheView& c, const AttnPlan& p, const uint16_t* q, fl
     return dispatch_g<8, 8, 0, false, kFmtFp8>(c, p, q, out, ws, st, occ);
   }
   if (c.fmt == kFmtSym32) return dispatch_kb<kFmtSym32>(c, p, q, out, ws, st, occ);
+  if (p.rope) return dispatch_kb<kFmtRope>(c, p, q, out, ws, st, occ);
   return dispatch_kb<kFmtInt>(c, p, q, out, ws, st, occ);
 }
 
@@ -1326,22 +1479,24 @@ hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p, const 
   return hipGetLastError();
 }
 
-int attention_blocks_per_cu(const CacheView& c, int group) {
+int attention_blocks_per_cu(const CacheView& c, int group, int rope) {
+  const bool p_rope = rope != 0;
   // cached per device and kernel variant (0 = not queried yet; threads may
   // race to fill an entry with the same value)
-  static std::atomic<int> cache[16][3][3][2][2][4][3];
+  static std::atomic<int> cache[16][3][3][2][2][4][4];
   const auto bi = [](int b) { return b == 2 ? 0 : (b == 4 ? 1 : 2); };
   const int gi = group == 1 ? 0 : (group == 2 ? 1 : (group == 4 ? 2 : 3));
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = -1;
   std::atomic<int>* slot =
-      dev >= 0 ? &cache[dev][bi(c.kbits)][bi(c.vbits)][c.kaxis ? 1 : 0][c.sparse ? 1 : 0][gi][c.fmt % 3] : nullptr;
+      dev >= 0 ? &cache[dev][bi(c.kbits)][bi(c.vbits)][c.kaxis ? 1 : 0][c.sparse ? 1 : 0][gi][p_rope ? 3 : c.fmt % 3] : nullptr;
   if (slot) {
     const int known = slot->load(std::memory_order_relaxed);
     if (known > 0) return known;
   }
   AttnPlan p{};
   p.group = group;
+  p.rope = rope;
   int occ = 0;
   if (dispatch(c, p, nullptr, nullptr, nullptr, nullptr, &occ) != hipSuccess || occ < 1) occ = 1;
   if (slot) slot->store(occ, std::memory_order_relaxed);

@@ -15,6 +15,9 @@ constexpr int kBlock = 32;   // tokens per key group / value code block
 // and zero point, fp8 E4M3 bytes with one scale per cache side, or symmetric
 // codes with one fp16 scale per 32-channel block of a token.
 enum : int { kFmtInt = 0, kFmtFp8 = 1, kFmtSym32 = 2 };
+// Attention only: affine codes whose channel-axis keys are cached before the
+// rotary position embedding, which the kernel applies after dequantization.
+constexpr int kFmtRope = 3;
 constexpr int kSymBlocks = 4;  // 32-channel blocks per token vector
 
 // Everything a kernel needs to address one layer's cache.
@@ -61,13 +64,15 @@ struct AttnPlan {
   int64_t units;               // 32-token tiles of all (sequence, KV head) pairs
   int n_wg;                    // attention workgroups (each takes units / n_wg)
   int need_combine;            // some pair spans several workgroups, or a sequence is empty
+  int rope;                    // keys cached before the rotary embedding
+  double rope_log2_theta;      // log2 of its frequency base
 };
 hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p,
                                    const uint16_t* q, float* out, float* ws,
                                    hipStream_t st);
-// Workgroups of the attention kernel variant for (c, group) resident per
-// compute unit (at least 1).
-int attention_blocks_per_cu(const CacheView& c, int group);
+// Workgroups of the attention kernel variant for (c, group, rotary keys)
+// resident per compute unit (at least 1).
+int attention_blocks_per_cu(const CacheView& c, int group, int rope);
 
 // Workspace: fp32 partial results [2 n_wg][G][kPartialFloats] = m, l, 2 pad,
 // o[128]: two slots per attention workgroup (the first and the last segment

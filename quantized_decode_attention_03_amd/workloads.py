@@ -50,6 +50,8 @@ class Spec:
     fmt: str = "int"         # element format: "int" (affine), "fp8" or "sym32"
     k_scale: float = 1.0     # fp8 per-cache scales
     v_scale: float = 1.0
+    k_rope: int = 0          # 1: keys cached before the rotary embedding
+    rope_theta: float = 10000.0
 
     @property
     def ragged(self):

@@ -14,7 +14,7 @@ ATOL = 2e-3   # attention tolerance, max-abs against the float64 oracle
 def ref_config(s):
     return RefConfig(s.d_head, s.n_kv_heads, s.n_q_heads, s.k_bits, s.v_bits, s.k_axis,
                      s.k_group, s.k_residual, s.k_sparse, k_format=s.fmt, v_format=s.fmt,
-                     k_scale=s.k_scale, v_scale=s.v_scale)
+                     k_scale=s.k_scale, v_scale=s.v_scale, k_rope=s.k_rope, rope_theta=s.rope_theta)
 
 
 def to_dev(a):

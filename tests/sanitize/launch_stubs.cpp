@@ -20,6 +20,6 @@ hipError_t launch_append_decode(const CacheView&, const AppendInputs&, hipStream
 hipError_t launch_dequantize(const CacheView&, uint16_t*, uint16_t*, hipStream_t) { reached("dequantize"); }
 hipError_t launch_decode_attention(const CacheView&, const AttnPlan&, const uint16_t*, float*, float*,
                                    hipStream_t) { reached("attention"); }
-int attention_blocks_per_cu(const CacheView&, int) { reached("occupancy"); }
+int attention_blocks_per_cu(const CacheView&, int, int) { reached("occupancy"); }
 
 }  // namespace kvq

@@ -98,6 +98,12 @@ def test_worked_example_nominal():
     (dict(TOKEN_AXIS, k_bits=8, v_bits=8, k_format="fp8", k_scale=0.0), N.KVQ_EINVAL),
     (dict(TOKEN_AXIS, k_bits=8, v_bits=8, k_format="fp8", v_scale=float("inf")), N.KVQ_EINVAL),
     (dict(TOKEN_AXIS, k_bits=8, v_bits=8, k_format="fp8", v_scale=float("nan")), N.KVQ_EINVAL),
+    # pre-RoPE keys: channel-axis affine keys without sparse entries, a base above 1
+    (dict(k_rope=2), N.KVQ_EINVAL),
+    (dict(k_rope=1, rope_theta=1.0), N.KVQ_EINVAL),
+    (dict(k_rope=1, rope_theta=float("nan")), N.KVQ_EINVAL),
+    (dict(TOKEN_AXIS, k_rope=1), N.KVQ_EUNSUPPORTED),
+    (dict(k_rope=1, k_sparse_per_vector=2), N.KVQ_EUNSUPPORTED),
 ])
 def test_bad_config(kw, status):
     c = _cfg(**kw)
@@ -105,6 +111,12 @@ def test_bad_config(kw, status):
         kvq_cache_sizes(c, 2, 256)
     assert e.value.status == status
     assert kvq_workspace_bytes(c, 2, 256) == 0
+
+
+def test_rope_config_accepted():
+    for kw in (dict(k_rope=1), dict(k_rope=1, k_bits=2, v_bits=2, k_residual_tokens=128, rope_theta=5e5)):
+        c = _cfg(**kw)
+        assert kvq_cache_sizes(c, 2, 256) == kvq_cache_sizes(_cfg(**{**kw, "k_rope": 0}), 2, 256)
 
 
 def test_unknown_format_code():

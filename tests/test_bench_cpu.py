@@ -183,13 +183,14 @@ def test_bench_formats_mode(monkeypatch, capsys):
     (shrunk here) and reports each one's bytes and roofline."""
     import json
     _stub_gpu(monkeypatch)
-    monkeypatch.setattr(W, "SPECS", {**W.SPECS, 3: replace(W.SPECS[3], seq_len=640, min_len=640)})
+    monkeypatch.setattr(W, "SPECS", {**W.SPECS, 3: replace(W.SPECS[3], seq_len=640, min_len=640),
+                                     2: replace(W.SPECS[2], batch=2, seq_len=300, min_len=300)})
     monkeypatch.setattr(sys, "argv", ["bench.py", "--formats", "--steps", "2", "--warmup", "1",
                                       "--settle-ms", "0"])
     bench.main()
     d = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
     ws = d["workloads"]
-    assert len(ws) == 4 and "cpu_baseline" not in d
+    assert len(ws) == 5 and "cpu_baseline" not in d and "pre-RoPE" in ws[4]["workload"]
     assert d["roofline"] == ws[0]["roofline"]
     # bytes per (token, KV head): int8 128+4+128+4, fp8 128+128, 8-bit blocks
     # 128+8+128+8, 4-bit blocks 64+8+64+8
