@@ -58,13 +58,69 @@ __device__ __forceinline__ uint2 quant_token(float f0, float f1, int fmt, int bi
     for (int off = 8; off >= 1; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off, 64));
     const uint16_t s16 = sym_scale16(a, bits);
     if ((lane & 15) == 0) reinterpret_cast<uint16_t*>(meta)[tok * kSymBlocks + (lane >> 4)] = s16;
-    const float sc = h2f(s16);
-    return make_uint2(sym_code(f0, sc, bits), sym_code(f1, sc, bits));
+    const float sc = h2f(s16), rc = __builtin_amdgcn_rcpf(sc);
+    return make_uint2(sym_code(f0, sc, rc, bits), sym_code(f1, sc, rc, bits));
   }
   const float mn = wave_min(__builtin_fminf(f0, f1)), mx = wave_max(__builtin_fmaxf(f0, f1));
   const GroupQ g = group_params(mn, mx, bits);
   if (lane == 0) meta[tok] = g.meta;
   return make_uint2(quant_code(f0, g, bits), quant_code(f1, g, bits));
+}
+
+// Stored codes u[0..7] of channels 8 l .. 8 l + 7 (values x) of one token
+// vector held by the 16 lanes l = lane mod 16 of a lane group, in the cache's
+// element format (the arithmetic of quant_token); the token's metadata goes
+// to slot `tok` of `meta` when `write` is set (lanes of a group that holds no
+// token compute on a copy and write nothing).
+__device__ __forceinline__ void quant_token8(const float (&x)[8], int fmt, int bits, float scale, uint32_t* meta,
+                                             size_t tok, int l, bool write, uint32_t (&u)[8]) {
+#pragma clang fp contract(off)
+  if (fmt == kFmtFp8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = e4m3_code(x[i] / scale);
+    return;
+  }
+  if (fmt == kFmtSym32) {  // a 32-channel block is 4 lanes
+    float a = __builtin_fabsf(x[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(x[i]));
+    a = __builtin_fmaxf(a, __shfl_xor(a, 1, 64));
+    a = __builtin_fmaxf(a, __shfl_xor(a, 2, 64));
+    const uint16_t s16 = sym_scale16(a, bits);
+    if (write && (l & 3) == 0) reinterpret_cast<uint16_t*>(meta)[tok * kSymBlocks + (l >> 2)] = s16;
+    const float sc = h2f(s16), rc = __builtin_amdgcn_rcpf(sc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = sym_code(x[i], sc, rc, bits);
+    return;
+  }
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    mn = __builtin_fminf(mn, x[i]);
+    mx = __builtin_fmaxf(mx, x[i]);
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) {
+    mn = __builtin_fminf(mn, __shfl_xor(mn, off, 64));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, off, 64));
+  }
+  const GroupQ g = group_params(mn, mx, bits);
+  if (write && l == 0) meta[tok] = g.meta;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) u[i] = quant_code(x[i], g, bits);
+}
+
+__device__ __forceinline__ void widen8(uint4 w, float (&x)[8]) {
+  const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = h2f((uint16_t)(a[i] & 0xFFFFu));
+    x[2 * i + 1] = h2f((uint16_t)(a[i] >> 16));
+  }
+}
+
+__device__ __forceinline__ uint2 pack8(const uint32_t (&u)[8]) {
+  return make_uint2(u[0] | (u[1] << 8) | (u[2] << 16) | (u[3] << 24), u[4] | (u[5] << 8) | (u[6] << 16) | (u[7] << 24));
 }
 
 // Sequence b's state before the append: L tokens held, its new tokens are
@@ -191,27 +247,46 @@ __global__ __launch_bounds__(256) void append_tokens_kernel(CacheView c, AppendI
   const bool ktok = c.kaxis == 0;
   const int Q2 = ktok ? L2 : L2 - L2 % c.R;
 
-  __shared__ uint8_t vcodes[kBlock][kD];
-  __shared__ uint8_t kcodes[kBlock][kD];
+  __shared__ __attribute__((aligned(16))) uint8_t vcodes[kBlock][kD];
+  __shared__ __attribute__((aligned(16))) uint8_t kcodes[kBlock][kD];
 
-  for (int tau = tlo + w; tau < thi; tau += 4) {
-    const int t = t0 + tau;
-    const size_t src = ((size_t)(row0 + t - L) * c.H + h) * kD;
-    {
-      const uint32_t pr = reinterpret_cast<const uint32_t*>(in.v_new + src)[lane];
-      const uint2 u = quant_token(h2f((uint16_t)(pr & 0xFFFFu)), h2f((uint16_t)(pr >> 16)), c.fmt, c.vbits,
-                                  c.vscale, c.v_meta, bh * c.T + t, lane);
-      vcodes[tau][2 * lane] = (uint8_t)u.x;
-      vcodes[tau][2 * lane + 1] = (uint8_t)u.y;
-    }
-    const uint32_t pk = reinterpret_cast<const uint32_t*>(in.k_new + src)[lane];
+  // Four token vectors per wavefront at a time: lane group q (16 lanes, 8
+  // channels each) takes token tlo + 16 r + 4 q + w in round r = 0, 1. Every
+  // load is issued first, at a clamped token index; groups past the last
+  // token compute on a copy and write nothing. (Keys only when they are
+  // quantized here, on the token axis; channel-axis keys are read by the
+  // flush, or below for the ones left in the window.)
+  const int q4 = lane >> 4, l16 = lane & 15;
+  uint4 vraw[2], kraw[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int tau = min(tlo + 16 * r + 4 * q4 + w, thi - 1);
+    const size_t src = ((size_t)(row0 + t0 + tau - L) * c.H + h) * kD + 8 * l16;
+    vraw[r] = *reinterpret_cast<const uint4*>(in.v_new + src);
+    kraw[r] = ktok ? *reinterpret_cast<const uint4*>(in.k_new + src) : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int tau = tlo + 16 * r + 4 * q4 + w;
+    const bool live = tau < thi;
+    const int tc = min(tau, thi - 1);
+    float x[8];
+    uint32_t u[8];
+    widen8(vraw[r], x);
+    quant_token8(x, c.fmt, c.vbits, c.vscale, c.v_meta, bh * c.T + t0 + tc, l16, live, u);
+    if (live) *reinterpret_cast<uint2*>(&vcodes[tau][8 * l16]) = pack8(u);
     if (ktok) {
-      const uint2 u = quant_token(h2f((uint16_t)(pk & 0xFFFFu)), h2f((uint16_t)(pk >> 16)), c.fmt, c.kbits,
-                                  c.kscale, c.k_meta, bh * c.T + t, lane);
-      kcodes[tau][2 * lane] = (uint8_t)u.x;
-      kcodes[tau][2 * lane + 1] = (uint8_t)u.y;
-    } else if (t >= Q2) {
-      reinterpret_cast<uint32_t*>(c.k_resid + (bh * c.R + (t - Q2)) * kD)[lane] = pk;
+      widen8(kraw[r], x);
+      quant_token8(x, c.fmt, c.kbits, c.kscale, c.k_meta, bh * c.T + t0 + tc, l16, live, u);
+      if (live) *reinterpret_cast<uint2*>(&kcodes[tau][8 * l16]) = pack8(u);
+    }
+  }
+  if (!ktok) {  // channel-axis keys that stay in the residual window
+    for (int tau = max(tlo, Q2 - t0) + w; tau < thi; tau += 4) {
+      const int t = t0 + tau;
+      const size_t src = ((size_t)(row0 + t - L) * c.H + h) * kD;
+      reinterpret_cast<uint32_t*>(c.k_resid + (bh * c.R + (t - Q2)) * kD)[lane] =
+          reinterpret_cast<const uint32_t*>(in.k_new + src)[lane];
     }
   }
   __syncthreads();

@@ -34,9 +34,24 @@ __host__ __device__ constexpr int qmax_of(int bits) { return (1 << (bits - 1)) -
 
 struct GroupQ {
   float s;      // scale as fp32 (exactly the stored fp16)
+  float r;      // its reciprocal, to within 1 ulp (for div_rint)
   float z;      // zero-point as fp32 (an integer in [-2048, 2048])
   uint32_t meta;  // fp16 scale bits | fp16 zero bits << 16
 };
+
+// rint(x / s) with x / s the correctly rounded fp32 quotient, given r =
+// 1/s to within 1 ulp. y = x * r is within 2^-22 |x/s| of that quotient, so
+// for |y| < 2^12 it is within 2^-10 of it: when y is more than 2^-9 from the
+// nearest half-integer both round to the same integer; otherwise (or for a
+// large quotient) the true division decides.
+__device__ __forceinline__ float div_rint(float x, float s, float r) {
+#pragma clang fp contract(off)
+  const float y = x * r;
+  const float k = __builtin_rintf(y);
+  const float d = __builtin_fabsf(y - k);
+  if (__builtin_fabsf(y) >= 4096.0f || __builtin_fabsf(d - 0.5f) < 0.001953125f) return __builtin_rintf(x / s);
+  return k;
+}
 
 // Scale and zero-point of a group from its fp32 extremes.
 __device__ __forceinline__ GroupQ group_params(float xmin, float xmax, int bits) {
@@ -64,6 +79,7 @@ __device__ __forceinline__ GroupQ group_params(float xmin, float xmax, int bits)
   }
   const float z = (float)qmin_of(bits) - r;
   g.z = z;
+  g.r = __builtin_amdgcn_rcpf(g.s);
   g.meta = (uint32_t)s16 | ((uint32_t)f2h_rne(z) << 16);
   return g;
 }
@@ -71,7 +87,7 @@ __device__ __forceinline__ GroupQ group_params(float xmin, float xmax, int bits)
 // Stored unsigned code u = q - q_min of one element.
 __device__ __forceinline__ uint32_t quant_code(float x, const GroupQ& g, int bits) {
 #pragma clang fp contract(off)
-  float q = __builtin_rintf(x / g.s) + g.z;
+  float q = div_rint(x, g.s, g.r) + g.z;
   q = __builtin_fminf(__builtin_fmaxf(q, (float)qmin_of(bits)), (float)qmax_of(bits));
   return (uint32_t)((int)q - qmin_of(bits));
 }
@@ -136,11 +152,12 @@ __device__ __forceinline__ uint16_t sym_scale16(float amax, int bits) {
   return f2h_up(amax / (float)qmax_of(bits));
 }
 
-// Stored code u = q - q_min of one element of a block with scale s.
-__device__ __forceinline__ uint32_t sym_code(float x, float s, int bits) {
+// Stored code u = q - q_min of one element of a block with scale s
+// (r = 1/s to within 1 ulp).
+__device__ __forceinline__ uint32_t sym_code(float x, float s, float r, int bits) {
 #pragma clang fp contract(off)
   const float qm = (float)qmax_of(bits);
-  const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(x / s), -qm), qm);
+  const float q = __builtin_fminf(__builtin_fmaxf(div_rint(x, s, r), -qm), qm);
   return (uint32_t)((int)q - qmin_of(bits));
 }
 

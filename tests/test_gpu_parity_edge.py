@@ -104,3 +104,50 @@ def test_offset_groups(cid):
     k[20:30] = (k[20:30].astype(f) * f(0.001) - f(40)).astype(F16)
     v[40:50] = (v[40:50].astype(f) * f(0.001) + f(25)).astype(F16)
     _run(s, k, v, lens, q)
+
+
+def _tie_vectors(rng, n, bits, d=128):
+    """n vectors of d fp16 values whose group (the vector) has x_min = q_min s
+    and x_max = q_max s with s a power of two (so the scale is exactly s),
+    every other element an exact half-integer multiple of s: a tie for the
+    rounding of x / s, decided by round-half-to-even."""
+    qmin, qmax = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    s = {8: 2.0 ** -6, 4: 2.0 ** -3, 2: 1.0}[bits]
+    k = rng.integers(qmin, qmax, size=(n, d))              # k + 0.5 in [q_min + 0.5, q_max - 0.5]
+    x = (k + 0.5) * s
+    x[:, 0], x[:, 1] = qmin * s, qmax * s
+    return x.astype(F16)
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+def test_exact_ties_token_groups(bits):
+    """Per-token groups full of exact ties, through the prefill path (four
+    tokens per wavefront) and the decode-step path (one per wavefront)."""
+    s = W.spec(3, layers=1, batch=2, seq_len=70, min_len=70, k_bits=bits, v_bits=bits)
+    rng = np.random.default_rng(31)
+    H = s.n_kv_heads
+    k = _tie_vectors(rng, 140 * H, bits).reshape(140, H, 128)
+    v = _tie_vectors(rng, 140 * H, bits).reshape(140, H, 128)
+    p = Pair(s, 96)
+    p.append(k, v, [70, 70])
+    for i in range(3):
+        p.append(_tie_vectors(rng, 2 * H, bits).reshape(2, H, 128), _tie_vectors(rng, 2 * H, bits).reshape(2, H, 128),
+                 [1, 1])
+    p.assert_state_equal()
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_exact_ties_channel_groups(bits):
+    """Channel-axis key groups (one channel over 32 tokens) full of exact
+    ties, through the residual flush."""
+    s = W.spec(2, batch=2, seq_len=64, min_len=64, k_bits=bits, v_bits=bits)
+    rng = np.random.default_rng(32)
+    H = s.n_kv_heads
+    # [token, head, channel]: per (head, channel) and 32-token block, token 0
+    # of the block q_min s, token 1 q_max s, the rest ties
+    kt = _tie_vectors(rng, 2 * H * 128 * 2, bits, d=32).reshape(2, H, 128, 2, 32)   # [b, h, c, blk, tok]
+    k = kt.transpose(0, 3, 4, 1, 2).reshape(128, H, 128)
+    v = _tie_vectors(rng, 128 * H, bits).reshape(128, H, 128)
+    p = Pair(s, 128)
+    p.append(k, v, [64, 64])
+    p.assert_state_equal()
