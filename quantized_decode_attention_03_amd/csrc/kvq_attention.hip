@@ -1307,13 +1307,15 @@ __global__ __launch_bounds__(256) void combine_kernel(CacheView c, AttnPlan p, c
   __shared__ float other[3][kD];  // the second half's (M, l, o)
   const int bq = blockIdx.x, t = threadIdx.x, ch = t & (kD - 1), half = t >> 7;
   const int b = bq / p.Hq, hkv = (bq % p.Hq) / p.group, hh = bq % p.group;
+  // the length and the units before the sequence: loads issued together
   const int L = seq_len_of(c, b);
+  const int before = units_before(c, b);
   if (L == 0) {
     if (half == 0) out[(size_t)bq * kD + ch] = 0.f;
     return;
   }
   const int nt = units_of(c, L);
-  const int s0 = units_before(c, b) + hkv * nt;  // the pair's units [s0, s0 + nt)
+  const int s0 = before + hkv * nt;  // the pair's units [s0, s0 + nt)
   const int first = wg_of_unit(s0, p.units, p.n_wg), last = wg_of_unit(s0 + nt - 1, p.units, p.n_wg);
   const int np = last - first + 1;
   if (np <= 1) return;  // written by the attention kernel
