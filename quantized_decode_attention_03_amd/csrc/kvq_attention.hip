@@ -70,6 +70,7 @@
 // device-scope fences, whose L2 writeback and invalidation cost far more than
 // the extra launch on this chip.)
 #include <algorithm>
+#include <type_traits>
 #include <atomic>
 
 #include "kvq_device.h"
@@ -1298,12 +1299,13 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
 // whose output the attention kernel did not write: sequences with no tokens
 // (output 0) and pairs whose units span several workgroups, whose partial
 // results it merges with a log-sum-exp. Thread t takes channel t mod 128 and
-// every second partial (t / 128 says which): it loads kChunk partials' (m, l,
-// o[channel]) at once, so one round trip to memory covers 2 kChunk partials,
-// merges them in registers, and the two halves meet in LDS.
+// every second partial (t / 128 says which): it loads a batch of partials'
+// (m, l, o[channel]) at once (4, or 32 when the pair has more than 8 pieces),
+// so one round trip to memory covers a whole batch, merges them in registers,
+// and the two halves meet in LDS.
 __global__ __launch_bounds__(256) void combine_kernel(CacheView c, AttnPlan p, const float* __restrict__ ws,
                                                       float* __restrict__ out) {
-  constexpr int kChunk = 32;
+  constexpr int kChunk = 32, kSmallChunk = 4;
   __shared__ float other[3][kD];  // the second half's (M, l, o)
   const int bq = blockIdx.x, t = threadIdx.x, ch = t & (kD - 1), half = t >> 7;
   const int b = bq / p.Hq, hkv = (bq % p.Hq) / p.group, hh = bq % p.group;
@@ -1327,36 +1329,44 @@ __global__ __launch_bounds__(256) void combine_kernel(CacheView c, AttnPlan p, c
     return ws + ((size_t)slot * p.group + hh) * kPartialFloats;
   };
   float M = -INFINITY, o = 0.f, l = 0.f;
-  for (int j0 = half; j0 < np; j0 += 2 * kChunk) {
-    float mv[kChunk], lv[kChunk], ov[kChunk];
-    // loads of a clamped index, unconditional, so that all of them are in
-    // flight together; entries past the last partial are masked afterwards
+  // merge the partials j = half, half + 2, ... in batches of C
+  auto merge = [&](auto chunk) {
+    constexpr int C = decltype(chunk)::value;
+    for (int j0 = half; j0 < np; j0 += 2 * C) {
+      float mv[C], lv[C], ov[C];
+      // loads of a clamped index, unconditional, so that all of them are in
+      // flight together; entries past the last partial are masked afterwards
 #pragma unroll
-    for (int y = 0; y < kChunk; ++y) {
-      const float* pt = rec(min(j0 + 2 * y, np - 1));
-      mv[y] = pt[0];
-      lv[y] = pt[1];
-      ov[y] = pt[4 + ch];
+      for (int y = 0; y < C; ++y) {
+        const float* pt = rec(min(j0 + 2 * y, np - 1));
+        mv[y] = pt[0];
+        lv[y] = pt[1];
+        ov[y] = pt[4 + ch];
+      }
+#pragma unroll
+      for (int y = 0; y < C; ++y)
+        if (j0 + 2 * y >= np) mv[y] = -INFINITY;
+      float mb = mv[0];
+#pragma unroll
+      for (int y = 1; y < C; ++y) mb = fmaxf(mb, mv[y]);
+      const float m_new = fmaxf(M, mb);
+      if (m_new == -INFINITY) continue;
+      const float fo = __builtin_amdgcn_exp2f(M - m_new);
+      o *= fo;
+      l *= fo;
+#pragma unroll
+      for (int y = 0; y < C; ++y) {  // an absent or empty partial weighs exp2(-inf) = 0
+        const float f = __builtin_amdgcn_exp2f(mv[y] - m_new);
+        o = __builtin_fmaf(f, ov[y], o);
+        l = __builtin_fmaf(f, lv[y], l);
+      }
+      M = m_new;
     }
-#pragma unroll
-    for (int y = 0; y < kChunk; ++y)
-      if (j0 + 2 * y >= np) mv[y] = -INFINITY;
-    float mb = mv[0];
-#pragma unroll
-    for (int y = 1; y < kChunk; ++y) mb = fmaxf(mb, mv[y]);
-    const float m_new = fmaxf(M, mb);
-    if (m_new == -INFINITY) continue;
-    const float fo = __builtin_amdgcn_exp2f(M - m_new);
-    o *= fo;
-    l *= fo;
-#pragma unroll
-    for (int y = 0; y < kChunk; ++y) {  // an absent or empty partial weighs exp2(-inf) = 0
-      const float f = __builtin_amdgcn_exp2f(mv[y] - m_new);
-      o = __builtin_fmaf(f, ov[y], o);
-      l = __builtin_fmaf(f, lv[y], l);
-    }
-    M = m_new;
-  }
+  };
+  // most pairs span a few workgroups: a small batch then avoids issuing
+  // dozens of redundant loads per thread
+  if (np <= 2 * kSmallChunk) merge(std::integral_constant<int, kSmallChunk>{});
+  else merge(std::integral_constant<int, kChunk>{});
   if (half == 1) {
     other[0][ch] = M;
     other[1][ch] = l;
