@@ -589,7 +589,8 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   constexpr int kMerge = (int)sizeof(MergeLds<G>);
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMain > kMerge ? kMain : kMerge];
   // query heads pre-scaled for the sparse entries (written identically by every wavefront)
-  __shared__ float qsh[SPARSE ? G : 1][SPARSE ? kD : 1];
+  // (rows padded by one word: the heads' copies of a channel fall in different banks)
+  __shared__ float qsh[SPARSE ? G : 1][SPARSE ? kD + 1 : 1];
   // rotary keys: revolutions per token of frequency i, theta_i / (2 pi) with
   // theta_i = base^(-i / 64), as two floats (computed in double)
   __shared__ float2 rphi[kRope ? 64 : 1];
@@ -927,6 +928,24 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           vm[4 * x] = a.x; vm[4 * x + 1] = a.y; vm[4 * x + 2] = a.z; vm[4 * x + 3] = a.w;
         }
       }
+      // sparse key entries of the lane's tokens 8grp .. 8grp + 7 and the
+      // scaled query at their channels, read before the key product (whose
+      // LDS fences would otherwise hold these reads back until after it)
+      float spq[SPARSE ? 16 : 1];
+      uint32_t spv[SPARSE ? 8 : 1];
+      if constexpr (SPARSE) {
+        uint32_t spc[8];
+#pragma unroll
+        for (int i2 = 0; i2 < 8; i2 += 2) {
+          const uint4 r2 = reinterpret_cast<const uint4*>(spr)[(8 * grp + i2) / 2];
+          spv[i2] = r2.x; spc[i2] = r2.y; spv[i2 + 1] = r2.z; spc[i2 + 1] = r2.w;
+        }
+#pragma unroll
+        for (int i2 = 0; i2 < 8; ++i2) {
+          spq[2 * i2] = qsh[hq][spc[i2] & 0xFFFFu];
+          spq[2 * i2 + 1] = qsh[hq][spc[i2] >> 16];
+        }
+      }
       // key codes of the lane's two A rows: bytes [grp*4KB, +4KB) of each row
       // (symmetric blocks: kc[e][j] / kc[e][2j, 2j+1] the words sym_key_frag
       // takes for block j)
@@ -1115,10 +1134,8 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
       }
       if constexpr (SPARSE) {
 #pragma unroll
-        for (int i2 = 0; i2 < 8; ++i2) {
-          const uint2 rec = reinterpret_cast<const uint2*>(spr)[8 * grp + i2];
-          sc[i2] += qsh[hq][rec.y & 0xFFFFu] * f16lo(rec.x) + qsh[hq][rec.y >> 16] * f16hi(rec.x);
-        }
+        for (int i2 = 0; i2 < 8; ++i2)
+          sc[i2] += spq[2 * i2] * f16lo(spv[i2]) + spq[2 * i2 + 1] * f16hi(spv[i2]);
       }
       // value codes: channel 16j + c16, tokens 8grp .. 8grp+7 of the block
       uint32_t vcl[8], vch[8];
