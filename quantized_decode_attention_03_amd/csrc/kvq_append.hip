@@ -336,41 +336,57 @@ __global__ __launch_bounds__(256) void append_decode_kernel(CacheView c, AppendI
   const bool ktok = c.kaxis == 0;
   const int Q2 = ktok ? L2 : L2 - L2 % c.R;
   const int j = t / kBlock, tau = t % kBlock;
-  for (int h = w; h < c.H; h += 4) {
-    const size_t bh = (size_t)b * c.H + h;
-    const size_t src = ((size_t)sn.row0 * c.H + h) * kD;
-    const uint32_t pr = reinterpret_cast<const uint32_t*>(in.v_new + src)[lane];
-    const uint32_t pk = reinterpret_cast<const uint32_t*>(in.k_new + src)[lane];
-    {  // value codes of channels 2 lane and 2 lane + 1 into their records
-      const uint2 u = quant_token(h2f((uint16_t)(pr & 0xFFFFu)), h2f((uint16_t)(pr >> 16)), c.fmt, c.vbits,
-                                  c.vscale, c.v_meta, bh * c.T + t, lane);
-      const uint32_t u0 = u.x, u1 = u.y;
-      const int vb = c.vbits, per = 32 / vb, wd = tau / per, f = tau % per;
-      // fields of earlier tokens in the word are kept, later ones are zero
-      const uint32_t keep = (1u << (f * vb)) - 1u;
-      uint32_t* rec = reinterpret_cast<uint32_t*>(c.v_codes + (bh * (c.T / kBlock) + j) * (size_t)(kD * 4 * vb));
-      uint32_t* p0 = rec + (2 * lane) * vb + wd;
-      uint32_t* p1 = rec + (2 * lane + 1) * vb + wd;
-      const uint32_t o0 = f ? *p0 : 0u, o1 = f ? *p1 : 0u;
-      *p0 = (o0 & keep) | (u0 << (f * vb));
-      *p1 = (o1 & keep) | (u1 << (f * vb));
+  const int vb = c.vbits, per = 32 / vb, wd = tau / per, f = tau % per;
+  // fields of earlier tokens in a value-record word are kept, later ones are
+  // zero (keep = 0 for the first token of a word)
+  const uint32_t keep = (1u << (f * vb)) - 1u;
+  // This wavefront's heads w, w + 4, ..., two at a time: every load first (the
+  // new token's key and value rows and the two value-record words per lane it
+  // extends; a clamped head index for the second when there is none), then the
+  // quantization and the stores.
+  for (int h0 = w; h0 < c.H; h0 += 8) {
+    uint32_t pr[2], pk[2], o0[2], o1[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int h = min(h0 + 4 * x, c.H - 1);
+      const size_t bh = (size_t)b * c.H + h;
+      const size_t src = ((size_t)sn.row0 * c.H + h) * kD;
+      pr[x] = reinterpret_cast<const uint32_t*>(in.v_new + src)[lane];
+      pk[x] = reinterpret_cast<const uint32_t*>(in.k_new + src)[lane];
+      const uint32_t* rec =
+          reinterpret_cast<const uint32_t*>(c.v_codes + (bh * (c.T / kBlock) + j) * (size_t)(kD * 4 * vb));
+      o0[x] = rec[(2 * lane) * vb + wd];
+      o1[x] = rec[(2 * lane + 1) * vb + wd];
     }
-    if (ktok) {  // the token's key row, channels packed low bits first
-      const uint2 u = quant_token(h2f((uint16_t)(pk & 0xFFFFu)), h2f((uint16_t)(pk >> 16)), c.fmt, c.kbits,
-                                  c.kscale, c.k_meta, bh * c.T + t, lane);
-      const uint32_t u0 = u.x, u1 = u.y;
-      uint8_t* row = c.k_codes + (bh * c.T + t) * (size_t)(16 * c.kbits);
-      if (c.kbits == 8) {
-        reinterpret_cast<uint16_t*>(row)[lane] = (uint16_t)(u0 | (u1 << 8));
-      } else if (c.kbits == 4) {
-        row[lane] = (uint8_t)(u0 | (u1 << 4));
-      } else {  // byte m holds channels 4m .. 4m+3: lanes 2m and 2m + 1
-        const uint32_t v = u0 | (u1 << 2);
-        const uint32_t o = (uint32_t)__shfl_xor((int)v, 1, 64);
-        if ((lane & 1) == 0) row[lane >> 1] = (uint8_t)(v | (o << 4));
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int h = h0 + 4 * x;
+      if (h >= c.H) break;
+      const size_t bh = (size_t)b * c.H + h;
+      {  // value codes of channels 2 lane and 2 lane + 1 into their records
+        const uint2 u = quant_token(h2f((uint16_t)(pr[x] & 0xFFFFu)), h2f((uint16_t)(pr[x] >> 16)), c.fmt, c.vbits,
+                                    c.vscale, c.v_meta, bh * c.T + t, lane);
+        uint32_t* rec = reinterpret_cast<uint32_t*>(c.v_codes + (bh * (c.T / kBlock) + j) * (size_t)(kD * 4 * vb));
+        rec[(2 * lane) * vb + wd] = (o0[x] & keep) | (u.x << (f * vb));
+        rec[(2 * lane + 1) * vb + wd] = (o1[x] & keep) | (u.y << (f * vb));
       }
-    } else if (t >= Q2) {
-      reinterpret_cast<uint32_t*>(c.k_resid + (bh * c.R + (t - Q2)) * kD)[lane] = pk;
+      if (ktok) {  // the token's key row, channels packed low bits first
+        const uint2 u = quant_token(h2f((uint16_t)(pk[x] & 0xFFFFu)), h2f((uint16_t)(pk[x] >> 16)), c.fmt, c.kbits,
+                                    c.kscale, c.k_meta, bh * c.T + t, lane);
+        const uint32_t u0 = u.x, u1 = u.y;
+        uint8_t* row = c.k_codes + (bh * c.T + t) * (size_t)(16 * c.kbits);
+        if (c.kbits == 8) {
+          reinterpret_cast<uint16_t*>(row)[lane] = (uint16_t)(u0 | (u1 << 8));
+        } else if (c.kbits == 4) {
+          row[lane] = (uint8_t)(u0 | (u1 << 4));
+        } else {  // byte m holds channels 4m .. 4m+3: lanes 2m and 2m + 1
+          const uint32_t v = u0 | (u1 << 2);
+          const uint32_t o = (uint32_t)__shfl_xor((int)v, 1, 64);
+          if ((lane & 1) == 0) row[lane >> 1] = (uint8_t)(v | (o << 4));
+        }
+      } else if (t >= Q2) {
+        reinterpret_cast<uint32_t*>(c.k_resid + (bh * c.R + (t - Q2)) * kD)[lane] = pk[x];
+      }
     }
   }
   __syncthreads();  // every wavefront has read the old length
