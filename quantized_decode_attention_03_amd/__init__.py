@@ -135,6 +135,7 @@ class KVCache:
             ctypes.cast(ctypes.c_void_p(self.seq_len.data_ptr()), ctypes.POINTER(ctypes.c_int32)),
             ctypes.cast(self.len_host, ctypes.POINTER(ctypes.c_int32)))
         self._cfg = cfg.c()
+        self._n_prev, self._n_arr = None, None   # last host counts passed to kvq_append
 
     def lengths(self):
         return list(self.len_host)
@@ -185,10 +186,10 @@ def kvq_append(cache, k_new, v_new, cu_new, n_new, stream=None):
     of their prefix offsets (None: built here from n_new); n_new: host
     sequence of B ints."""
     import torch
-    n_list = [int(x) for x in n_new]
+    n_list = n_new if type(n_new) is list else [int(x) for x in n_new]
     if len(n_list) != cache.batch:
         raise ValueError(f"n_new: {len(n_list)} counts for a batch of {cache.batch}")
-    if any(x < 0 for x in n_list):
+    if cache.batch and min(n_list) < 0:
         raise ValueError("n_new: negative count")
     cfg, dev = cache.cfg, cache.device
     rows = (sum(n_list), cfg.n_kv_heads, cfg.d_head)
@@ -200,12 +201,12 @@ def kvq_append(cache, k_new, v_new, cu_new, n_new, stream=None):
             cu.append(cu[-1] + x)
         cu_new = torch.tensor(cu, dtype=torch.int32, device=dev)
     _check(cu_new, "cu_new", torch.int32, (cache.batch + 1,), dev)
-    n = (ctypes.c_int32 * cache.batch)(*n_list)
-    N.check(N.lib().kvq_append(ctypes.byref(cache._cfg), ctypes.byref(cache._c), _ptr(k_new),
-                               _ptr(v_new),
-                               ctypes.cast(ctypes.c_void_p(cu_new.data_ptr()),
-                                           ctypes.POINTER(ctypes.c_int32)),
-                               n, _stream(stream)), "kvq_append")
+    # the host counts as a C array, kept while they repeat (every decode step)
+    if n_list != cache._n_prev:
+        cache._n_arr = (ctypes.c_int32 * cache.batch)(*n_list)
+        cache._n_prev = list(n_list)
+    N.check(N.lib().kvq_append(ctypes.byref(cache._cfg), ctypes.byref(cache._c), _ptr(k_new), _ptr(v_new),
+                               _ptr(cu_new), cache._n_arr, _stream(stream)), "kvq_append")
 
 
 def kvq_decode_attention(cache, q, out, softmax_scale, ws, stream=None):

@@ -65,7 +65,7 @@ def lib():
         L.kvq_cache_sizes.restype = ctypes.c_int
         L.kvq_workspace_bytes.argtypes = [cp(kvq_config), i32, i64]
         L.kvq_workspace_bytes.restype = ctypes.c_size_t
-        L.kvq_append.argtypes = [cp(kvq_config), cp(kvq_cache), vp, vp, i32p, i32p, vp]
+        L.kvq_append.argtypes = [cp(kvq_config), cp(kvq_cache), vp, vp, vp, i32p, vp]
         L.kvq_append.restype = ctypes.c_int
         L.kvq_decode_attention.argtypes = [cp(kvq_config), cp(kvq_cache), vp, vp, ctypes.c_float,
                                            vp, ctypes.c_size_t, vp]

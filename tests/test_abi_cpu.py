@@ -291,3 +291,45 @@ def test_binding_check_rules(monkeypatch):
         K._check(dev(torch.zeros((8, 4, 128), dtype=torch.float16)).transpose(0, 1), "t", torch.float16)
     with pytest.raises(ValueError, match="the cache is on"):
         K._check(t, "t", torch.float16, None, torch.device("cuda", 1))
+
+
+def test_append_binding_passes_current_counts(monkeypatch):
+    """The binding keeps the C array of host counts while the counts repeat
+    (every decode step); a change of counts, also in place in the same list,
+    reaches the library."""
+    import quantized_decode_attention_03_amd as K
+    seen = []
+
+    class Lib:
+        def kvq_append(self, cfg, cache, k, v, cu, n, stream):
+            seen.append(list(n))
+            return N.KVQ_OK
+
+    monkeypatch.setattr(N, "lib", lambda: Lib())
+    monkeypatch.setattr(K, "_check", lambda *a, **k: None)
+
+    class Stream:
+        cuda_stream = 0
+
+    class Cache:
+        batch, cfg, device = 3, _cfg(), None
+        _cfg, _c = None, None
+        _n_prev, _n_arr = None, None
+
+    class Buf:  # stands for a device tensor: only its address is read
+        def data_ptr(self):
+            return 1 << 20
+
+    c = Cache()
+    c._cfg, c._c = c.cfg.c(), N.kvq_cache()
+    counts = [1, 1, 1]
+    K.kvq_append(c, None, None, Buf(), counts, Stream())
+    K.kvq_append(c, None, None, Buf(), counts, Stream())
+    counts[1] = 5
+    K.kvq_append(c, None, None, Buf(), counts, Stream())
+    K.kvq_append(c, None, None, Buf(), (2, 0, 7), Stream())
+    assert seen == [[1, 1, 1], [1, 1, 1], [1, 5, 1], [2, 0, 7]]
+    with pytest.raises(ValueError):
+        K.kvq_append(c, None, None, Buf(), [1, -1, 1], Stream())
+    with pytest.raises(ValueError):
+        K.kvq_append(c, None, None, Buf(), [1, 1], Stream())
