@@ -16,19 +16,22 @@
 // Codes enter the matrix cores as their own bit patterns: a stored code u
 // masked at bit sh of an fp16 half (sh + bits <= 10) is the subnormal
 // u * 2^(sh-24), which the matrix cores multiply exactly. Chains of
-// accumulating MFMAs have an absolute error floor, so the products must not be
-// small (measured: 2-bit codes at u * 2^-24 gave key-score errors near 2e-3,
-// at u * 2^-16 near 5e-6); every product is kept at the magnitude it has with
-// all codes at bit SH, the variant's code unit 2^(SH-24): SH is 8 for 2-bit,
-// 4 for 4-bit and 0 for 8-bit codes.
-//   Values: every pair of codes is moved to bit SH (a shift and a mask).
+// accumulating MFMAs have an absolute error floor, so the key products must
+// not be small (measured: 2-bit codes at u * 2^-24 gave key-score errors near
+// 2e-3, at u * 2^-16 near 5e-6); every key product is kept at the magnitude
+// it has with all codes at bit SH, the variant's code unit 2^(SH-24): SH is 8
+// for 2-bit, 4 for 4-bit and 0 for 8-bit codes.
 //   Channel-axis keys: each pair stays where a single mask reaches it (plus
 //     one shift per word for the fields above bit 10), and the factor
 //     2^(SH - sh) is folded into the scaled query of its channel, which has
-//     the fp16 range to spare (the softmax weights, the value product's other
-//     operand, do not).
+//     the fp16 range to spare.
 //   Token-axis keys: their query operand is the raw fp16 query, which cannot
-//     absorb a factor without rounding, so they take the value treatment.
+//     absorb a factor without rounding, so every pair is moved to bit SH.
+//   Values: each pair also stays where a single mask reaches it, and its
+//     softmax weights carry the factor 2^-sh (taken into the exponent), so
+//     every product is P * u * 2^-24. Factors at most 1 keep P inside fp16,
+//     and the value product is far less sensitive to the floor (measured:
+//     error / sum of P near 2e-5 with codes at u * 2^-24).
 //
 // Zero points are not subtracted element by element:
 //   keys, channel axis: x = s_c (u - z'_c); B = q * s_c (scaled query, split
@@ -37,9 +40,10 @@
 //     rows all hold -z');
 //   keys, token axis: x = s_t (u - z'_t); B = raw fp16 query (exact); the
 //     term z'_t * sum_c q_c is one FMA per score; s_t multiplies the score;
-//   values, token axis: x = s_t (u - z'_t); P = p_t * s_t * 2^kv as hi/lo rows
-//     h and g + h; the product with a B operand whose columns all hold z'_t
-//     is subtracted once at the end.
+//   values, token axis: x = s_t (u - z'_t); P = p_t * s_t * 2^kv (times the
+//     pair factor) as hi/lo rows h and g + h; the product with a B operand
+//     whose columns all hold z'_t (at the pair's bit) is subtracted once at
+//     the end.
 // The two other element formats keep keys on the token axis:
 //   fp8 E4M3: bytes become fp16 operands exactly (a hardware conversion; every
 //     E4M3 value is an fp16 value); the per-cache key scale multiplies the
@@ -124,6 +128,24 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+// Maximum of the 8 scores of a lane. The NaN-propagating maximum becomes
+// v_maximum3_f32 with no canonicalizing maximum in front of each operand (which
+// fmaxf takes for operands the compiler cannot prove canonical). Compiler
+// built-ins, not inline assembly: scores can come straight from the matrix
+// cores, and only compiler-emitted reads get the wait states that requires.
+__device__ __forceinline__ float max8(const float (&v)[8]) {
+  const auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+  return mx(mx(mx(v[0], v[1]), mx(v[2], v[3])), mx(mx(v[4], v[5]), mx(v[6], v[7])));
+}
+
+// -1 that the compiler cannot fold: x * -1 + y then stays one v_fma_mix_f32
+// with an fp16 operand instead of a conversion and a subtraction.
+__device__ __forceinline__ float opaque_neg1() {
+  float r = -1.f;
+  asm("" : "+s"(r));
+  return r;
 }
 
 // fp16 pair (RTZ) of two floats.
@@ -224,12 +246,20 @@ __device__ __forceinline__ Frag key_frag(const uint32_t* kc, int j) {
   return f;
 }
 
-// Value operand: 8 tokens of one channel, every code at bit SH. k-slot pair
-// p holds tokens (p, p+4) for 4/2-bit values, (2p, 2p+1) for 8-bit ones.
-//   4-bit: the record word (nibble i = token i), nibbles (p, p+4);
-//   2-bit: the 16-bit record spread to bytes 1 and 3 (tokens 0..3, 4..7),
-//          fields (8 + 2p, 24 + 2p);
+// Value operand: 8 tokens of one channel. k-slot pair p holds tokens (p,
+// p+4) for 4/2-bit values, (2p, 2p+1) for 8-bit ones, each pair where one mask
+// reaches it: codes at bit val_sh<VB>(p) of each half, the subnormal
+// u * 2^(val_sh - 24). The P operand of pair p carries the factor 2^-val_sh
+// (folded into its softmax weights), so every product is P * u * 2^-24.
+//   4-bit: the record word (nibble i = token i); nibbles (p, p+4) masked in
+//          place for p = 0, 1 (bits 0 and 4), after one shift by 8 for p = 2, 3;
+//   2-bit: the 16-bit record spread to bytes 0 and 2 (tokens 0..3, 4..7),
+//          fields (2p, 16 + 2p) masked in place;
 //   8-bit: bytes of two words.
+template <int VB>
+__host__ __device__ constexpr int val_sh(int p) {
+  return VB == 2 ? 2 * p : (VB == 4 ? 4 * (p & 1) : 0);
+}
 template <int VB>
 __device__ __forceinline__ Frag val_frag(uint32_t a, uint32_t b) {
   Frag f;
@@ -239,17 +269,23 @@ __device__ __forceinline__ Frag val_frag(uint32_t a, uint32_t b) {
     f.p[2] = perm(0u, b, 0x0C010C00u);
     f.p[3] = perm(0u, b, 0x0C030C02u);
   } else if constexpr (VB == 4) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) f.p[p] = field_pair<4>(a, 4 * p);
+    const uint32_t t = a >> 8;
+    f.p[0] = a & 0x000F000Fu;
+    f.p[1] = a & 0x00F000F0u;
+    f.p[2] = t & 0x000F000Fu;
+    f.p[3] = t & 0x00F000F0u;
   } else {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) f.p[p] = field_pair<2>(a, 8 + 2 * p);
+    for (int p = 0; p < 4; ++p) f.p[p] = a & (0x00030003u << (2 * p));
   }
   return f;
 }
 // The lane's value record words of one channel, as val_frag takes them.
+// 2-bit records are 16 bits, half of the aligned word at rec + 4 (grp / 2):
+// sel2 spreads the lane's half to bytes 0 and 2 (0x0C010C00 for even lane
+// groups, 0x0C030C02 for odd ones).
 template <int VB>
-__device__ __forceinline__ void val_words(const uint8_t* rec, int grp, uint32_t& lo, uint32_t& hi) {
+__device__ __forceinline__ void val_words(const uint8_t* rec, int grp, uint32_t sel2, uint32_t& lo, uint32_t& hi) {
   if constexpr (VB == 4) {
     lo = reinterpret_cast<const uint32_t*>(rec)[grp];
     hi = 0u;
@@ -258,7 +294,7 @@ __device__ __forceinline__ void val_words(const uint8_t* rec, int grp, uint32_t&
     lo = x.x;
     hi = x.y;
   } else {
-    lo = perm(0u, reinterpret_cast<const uint16_t*>(rec)[grp], 0x010C000Cu);
+    lo = perm(0u, reinterpret_cast<const uint32_t*>(rec)[grp >> 1], sel2);
     hi = 0u;
   }
 }
@@ -323,8 +359,9 @@ __device__ __forceinline__ void rope_cs(float t, float2 ph, float& c, float& s) 
 // fp16 hi and lo parts of two floats (y - hi is exact): the A operands of two
 // products whose sum keeps about 22 bits of y.
 __device__ __forceinline__ void split_hilo(float y0, float y1, uint32_t& hi, uint32_t& lo) {
+  const float m1 = opaque_neg1();
   hi = pk_rtz(y0, y1);
-  lo = pk_rtz(y0 - f16lo(hi), y1 - f16hi(hi));
+  lo = pk_rtz(__builtin_fmaf(f16lo(hi), m1, y0), __builtin_fmaf(f16hi(hi), m1, y1));
 }
 
 // Geometry of one 32-token tile as staged in LDS:
@@ -558,18 +595,17 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   constexpr bool kPermV = VB != 8;  // k-slot pairs (i, i+4) for 4/2-bit values
   static_assert(2 * G <= 16, "hi/lo rows must fit 16");
   // unit of one code step in the key / value operands, and its inverse
-  constexpr int kShK = unit_shift<KB>(), kShV = unit_shift<VB>();
+  constexpr int kShK = unit_shift<KB>();
   constexpr float kUnitK = pow2f(kShK - 24), kInvUnitK = pow2f(24 - kShK);
   // The value-scale factor 2^kv, kv = kKvTop - E, is set from the largest fp16
   // biased exponent E among the value scales seen so far, so that s * 2^kv <
   // 2^6 and the P operand p * s * 2^kv < 2^14 stays inside fp16.
   constexpr int kKvTop = 20;
-  constexpr _Float16 kZv = (_Float16)pow2f(kShV - 24);                // value code step
-  constexpr _Float16 kZvOfs = (_Float16)(-kQMinV * pow2f(kShV - 24));  // -q_min in code steps
   // symmetric blocks: x = s (u + q_min), so the zero point in code steps is
-  // -q_min for every token: a constant B operand
-  const Frag bsym = {{(uint32_t)(-kQMinV << kShV) * 0x10001u, (uint32_t)(-kQMinV << kShV) * 0x10001u,
-                      (uint32_t)(-kQMinV << kShV) * 0x10001u, (uint32_t)(-kQMinV << kShV) * 0x10001u}};
+  // -q_min for every token: a constant B operand (pair p at bit val_sh(p),
+  // like the codes it goes with)
+  const Frag bsym = {{(uint32_t)(-kQMinV << val_sh<VB>(0)) * 0x10001u, (uint32_t)(-kQMinV << val_sh<VB>(1)) * 0x10001u,
+                      (uint32_t)(-kQMinV << val_sh<VB>(2)) * 0x10001u, (uint32_t)(-kQMinV << val_sh<VB>(3)) * 0x10001u}};
   // value blocks feeding one P.V product (one per 32-channel block for
   // symmetric blocks, whose scales differ per block)
   constexpr int kPB = kSym ? kSymBlocks : 1;
@@ -583,6 +619,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
   const int brow = lo_col ? G + hq : hq;          // B-operand row this lane reads
   const float rowlo = lo_col ? 1.f : 0.f;         // lo rows of P
   const float qscale = p.scale * kLog2e;          // scores in log2 units
+  const uint32_t vsel2 = (grp & 1) ? 0x0C030C02u : 0x0C010C00u;  // 2-bit value records: this lane's half
 
   constexpr int kWaveBytes = NB * Gm::kBytes + Gm::kWaveLds;
   constexpr int kMain = 4 * kWaveBytes;
@@ -650,7 +687,8 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     const int ts0 = min(k0 * kBlock, Q), ts1 = min(k1 * kBlock, Q);
     // This wavefront's quantized tiles: k = w, w + 4, ... over [ts0, ts1).
     const int ntiles = (ts1 - ts0 + kBlock - 1) / kBlock;
-    const int nw = (w < ntiles) ? (ntiles - w + 3) / 4 : 0;
+    // (wave-uniform: made scalar so that the loop's waits and issues branch on SGPRs)
+    const int nw = __builtin_amdgcn_readfirstlane((w < ntiles) ? (ntiles - w + 3) / 4 : 0);
     // residual fp16 keys [Q, L): with the pair's last unit
     const int nres = (k1 == nt) ? (L - Q + kBlock - 1) / kBlock : 0;
 
@@ -774,14 +812,13 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     // words of channel chunk j.
     auto softmax_pv = [&](float (&sc)[8], float cs, const uint32_t (&vm)[kVmW], const uint32_t (&vcl)[8],
                           const uint32_t (&vch)[8], int t0, int tend) {
-      const int nvalid = tend - t0;
-      if (nvalid < kBlock) {
+      const int nvalid = __builtin_amdgcn_readfirstlane(tend - t0);
+      if (__builtin_expect(nvalid < kBlock, 0)) {  // a partial tile (rare): a branch, not 16 selects per tile
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if (8 * grp + i >= nvalid) sc[i] = -INFINITY;
       }
-      const float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                             fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      const float mx = max8(sc);
       if (__builtin_amdgcn_ballot_w64(__builtin_fmaf(mx, cs, -m_ref) > kLazy)) {
         const float m_new = fmaxf(m_ref, grp_max(mx * cs));
         const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -830,13 +867,16 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
           vE = e_new;
         }
       }
-      // fp8: P = p (at most 2^kLazy); otherwise P = p * s * 2^kv
+      // fp8: P = p (at most 2^kLazy); otherwise P = p * s * 2^kv; both times
+      // 2^-val_sh of the token's k-slot pair (the position of its value codes),
+      // taken into the exponent; l_run sums the weights p without it
       const float kvm = (kFp8 ? 0.f : (float)(kKvTop - vE)) - m_ref;
       float x[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cs, kvm));
-        l_run += x[i];
+        const int sh = val_sh<VB>(kPermV ? (i & 3) : (i >> 1));
+        x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cs, kvm - (float)sh));
+        l_run = __builtin_fmaf(x[i], __builtin_ldexpf(1.f, sh), l_run);
       }
       // the P operand from the 8 weights a[] of the lane's tokens; lo rows keep
       // P - fp16(P)
@@ -880,8 +920,10 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
         for (int pp = 0; pp < 4; ++pp) {
           const int i0 = kPermV ? pp : 2 * pp;
           const int i1 = kPermV ? pp + 4 : 2 * pp + 1;
-          // (z'_i0, z'_i1) in code steps, z' = z - qmin
-          bz.p[pp] = pk_fma16(perm(vm[i1], vm[i0], 0x07060302u), h2v{kZv, kZv}, h2v{kZvOfs, kZvOfs});
+          // (z'_i0, z'_i1) in code steps at the pair's bit, z' = z - qmin
+          const int sh = val_sh<VB>(pp);
+          const _Float16 zs = (_Float16)__builtin_ldexpf(1.f, sh - 24), zo = (_Float16)__builtin_ldexpf((float)-kQMinV, sh - 24);
+          bz.p[pp] = pk_fma16(perm(vm[i1], vm[i0], 0x07060302u), h2v{zs, zs}, h2v{zo, zo});
         }
         accz[0] = mfma(pf, bz, accz[0]);
 #pragma unroll
@@ -893,22 +935,23 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     // the per-channel scales in the low halves of km0, km1; with_zero also
     // writes the zero-point operand -(z - qmin) from their high halves
     auto build_qb = [&](uint32_t km0, uint32_t km1, bool with_zero) {
+      const float m1 = opaque_neg1();
       wave_lds_fence();
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         const float v0 = mul_lo(qv0[hh], km0), v1 = mul_lo(qv1[hh], km1);
         const uint32_t hi = pk_rtz(v0, v1);
         wl.qb[bg][hh][bj].p[bp] = hi;
-        wl.qb[bg][G + hh][bj].p[bp] = pk_rtz(__builtin_fmaf(f16lo(hi), -1.f, v0), __builtin_fmaf(f16hi(hi), -1.f, v1));
+        wl.qb[bg][G + hh][bj].p[bp] = pk_rtz(__builtin_fmaf(f16lo(hi), m1, v0), __builtin_fmaf(f16hi(hi), m1, v1));
       }
       if (with_zero) wl.zc[bg][bj][bp] = pk_fma16(perm(km1, km0, 0x07060302u), zmul, zofs);
       wave_lds_fence();
     };
 
     // ---- quantized tiles through the LDS pipeline -----------------------------
-    for (int i = 0; i < nw; ++i) {
-      const int slot = i % NB;
-      if (i + NB - 1 < nw) issue((i + NB - 1) % NB);
+    // Tile i sits in slot i mod NB.
+    auto tile = [&](const int i, const int slot) {
+      if (i + NB - 1 < nw) issue((slot + NB - 1) % NB);
       // tile i has landed once at most (tiles issued after it) x loads remain
       wait_vm_n<Gm::kLoads>(min(NB - 1, nw - 1 - i));
       const uint8_t* sb = wbase + slot * Gm::kBytes;
@@ -1140,9 +1183,10 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
       // value codes: channel 16j + c16, tokens 8grp .. 8grp+7 of the block
       uint32_t vcl[8], vch[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) val_words<VB>(vbuf + (16 * j + c16) * 4 * VB, grp, vcl[j], vch[j]);
+      for (int j = 0; j < 8; ++j) val_words<VB>(vbuf + (16 * j + c16) * 4 * VB, grp, vsel2, vcl[j], vch[j]);
       softmax_pv(sc, cs, vm, vcl, vch, t0, ts1);
-    }
+    };
+    for (int i = 0; i < nw; ++i) tile(i, i % NB);
 
 
     // ---- residual (fp16) key tiles, channel axis only: tile j holds tokens
@@ -1245,7 +1289,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
             vm[4] = bb.x; vm[5] = bb.y; vm[6] = bb.z; vm[7] = bb.w;
           }
 #pragma unroll
-          for (int j = 0; j < 8; ++j) val_words<VB>(vres_lds + (16 * j + c16) * 4 * VB, grp, vcl[j], vch[j]);
+          for (int j = 0; j < 8; ++j) val_words<VB>(vres_lds + (16 * j + c16) * 4 * VB, grp, vsel2, vcl[j], vch[j]);
           softmax_pv(sc, kRope ? qscale : 1.f, vm, vcl, vch, t0, L);
           wait_lgkm0();  // the keys are read before the next half's loads
           wave_lds_fence();
@@ -1256,7 +1300,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     // ---- merge the wavefronts of the workgroup ------------------------------
     // o = (acc - accz) / (value code unit) * 2^-kv, l = l_run * 2^-kv; fp8:
     // o = acc * (value scale), l = l_run
-    const float ofac = kFp8 ? c.vscale : __builtin_bit_cast(float, (uint32_t)(127 + 24 - kShV - kKvTop + vE) << 23);
+    const float ofac = kFp8 ? c.vscale : __builtin_bit_cast(float, (uint32_t)(127 + 24 - kKvTop + vE) << 23);
     const float lfac = kFp8 ? 1.f : __builtin_bit_cast(float, (uint32_t)(127 - kKvTop + vE) << 23);
     const float lsum = grp_sum(l_run) * lfac;
     wait_vm<0>();     // no tile load still writing LDS
@@ -1305,7 +1349,7 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
     if (k1 == nt && h == c.H - 1) {  // on to the next sequence with units (L > 0)
       base += c.H * nt;
       for (++b; b < c.B; ++b) {
-        L = seq_len_of(c, b);
+        L = __builtin_amdgcn_readfirstlane(seq_len_of(c, b));
         if (L > 0) break;
       }
     }

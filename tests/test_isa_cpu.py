@@ -17,6 +17,12 @@ hipcc cross-compiles to assembly here).
   sign-extended 32-bit value there would point the load far outside the
   cache). Traced through the register moves back to the definition, for every
   load of every kernel variant.
+* Inline assembly holds only the tile loads, the M0 set-up and the waits
+  (scalar instructions and buffer loads with an address operand): no vector
+  ALU instruction. The compiler inserts the wait states a vector read of a
+  matrix-core result needs only for instructions it emits itself, so an
+  inline-asm ALU operation on a score fresh from an MFMA would read stale
+  registers.
 * No kernel spills to scratch memory (a spill in the attention loop would add
   HBM traffic per tile).
 * Every kernel's LDS fits one compute unit (160 KiB).
@@ -81,6 +87,24 @@ def test_dma_loads_only_in_inline_asm(asm):
             inside = False
         elif re.search(r"_load_.*\blds\b", t) and not t.startswith(";"):
             assert inside, t
+
+
+def test_inline_asm_has_no_vector_alu(asm):
+    allowed = re.compile(r"(s_mov_b32 m0, s\d+|s_nop \d+|s_waitcnt (vmcnt|lgkmcnt)\(\d+\)|"
+                         r"buffer_load_dwordx4 v\d+, s\[\d+:\d+\], 0 offen lds)")
+    seen = 0
+    for src, text in asm.items():
+        inside = False
+        for line in text.split("\n"):
+            t = line.strip()
+            if t.startswith(";;#ASMSTART"):
+                inside = True
+            elif t.startswith(";;#ASMEND"):
+                inside = False
+            elif inside and t and not t.startswith(";"):
+                seen += 1
+                assert allowed.fullmatch(t), f"{src}: inline assembly outside the allowed forms: {t}"
+    assert seen > 0
 
 
 def test_dma_loads_are_range_checked(asm):
