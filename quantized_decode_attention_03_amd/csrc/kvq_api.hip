@@ -95,21 +95,20 @@ void plan_attention(const kvq_config* cfg, const kvq_cache* cache, int64_t slots
   nwg = std::min<int64_t>(nwg, kMaxWgs);
   p->units = U;
   p->n_wg = (int)nwg;
+  int64_t most = 1;  // the most workgroups one pair spans (the merge kernel's batch size follows it)
   if (nwg > 1) {
     int64_t base = 0;
-    for (int b = 0; b < cache->batch && !need; ++b) {
+    for (int b = 0; b < cache->batch; ++b) {
       const int64_t nt = units(b);
       for (int64_t h = 0; h < H && nt > 0; ++h) {
         const int64_t s0 = base + h * nt;
-        if (wg_of_unit_host(s0, U, nwg) != wg_of_unit_host(s0 + nt - 1, U, nwg)) {
-          need = true;
-          break;
-        }
+        most = std::max(most, wg_of_unit_host(s0 + nt - 1, U, nwg) - wg_of_unit_host(s0, U, nwg) + 1);
       }
       base += H * nt;
     }
   }
-  p->need_combine = need ? 1 : 0;
+  p->need_combine = (need || most > 1) ? 1 : 0;
+  p->max_pieces = (int)most;
 }
 
 kvq_status check_config(const kvq_config* cfg) {

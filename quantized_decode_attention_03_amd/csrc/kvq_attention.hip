@@ -1360,13 +1360,15 @@ __global__ __launch_bounds__(256) void attn_kernel(CacheView c, AttnPlan p, cons
 // whose output the attention kernel did not write: sequences with no tokens
 // (output 0) and pairs whose units span several workgroups, whose partial
 // results it merges with a log-sum-exp. Thread t takes channel t mod 128 and
-// every second partial (t / 128 says which): it loads a batch of partials'
-// (m, l, o[channel]) at once (4, or 32 when the pair has more than 8 pieces),
-// so one round trip to memory covers a whole batch, merges them in registers,
-// and the two halves meet in LDS.
+// every second partial (t / 128 says which): it loads a batch of C partials'
+// (m, l, o[channel]) at once, so one round trip to memory covers a whole
+// batch, merges them in registers, and the two halves meet in LDS. C is 4
+// when no pair has more than 8 pieces and 32 otherwise (a single long
+// sequence over many workgroups): the wide batch's registers would cut the
+// workgroups resident per compute unit for every launch.
+template <int C>
 __global__ __launch_bounds__(256) void combine_kernel(CacheView c, AttnPlan p, const float* __restrict__ ws,
                                                       float* __restrict__ out) {
-  constexpr int kChunk = 32, kSmallChunk = 4;
   __shared__ float other[3][kD];  // the second half's (M, l, o)
   const int bq = blockIdx.x, t = threadIdx.x, ch = t & (kD - 1), half = t >> 7;
   const int b = bq / p.Hq, hkv = (bq % p.Hq) / p.group, hh = bq % p.group;
@@ -1391,8 +1393,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CacheView c, AttnPlan p, c
   };
   float M = -INFINITY, o = 0.f, l = 0.f;
   // merge the partials j = half, half + 2, ... in batches of C
-  auto merge = [&](auto chunk) {
-    constexpr int C = decltype(chunk)::value;
+  {
     for (int j0 = half; j0 < np; j0 += 2 * C) {
       float mv[C], lv[C], ov[C];
       // loads of a clamped index, unconditional, so that all of them are in
@@ -1423,11 +1424,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CacheView c, AttnPlan p, c
       }
       M = m_new;
     }
-  };
-  // most pairs span a few workgroups: a small batch then avoids issuing
-  // dozens of redundant loads per thread
-  if (np <= 2 * kSmallChunk) merge(std::integral_constant<int, kSmallChunk>{});
-  else merge(std::integral_constant<int, kChunk>{});
+  }
   if (half == 1) {
     other[0][ch] = M;
     other[1][ch] = l;
@@ -1548,7 +1545,11 @@ hipError_t launch_decode_attention(const CacheView& c, const AttnPlan& p, const 
     if (e != hipSuccess) return e;
   }
   if (!p.need_combine) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(c.B * p.Hq), dim3(256), 0, st, c, p, ws, out);
+  constexpr int kSmallChunk = 4, kChunk = 32;
+  if (p.max_pieces <= 2 * kSmallChunk)
+    hipLaunchKernelGGL(combine_kernel<kSmallChunk>, dim3(c.B * p.Hq), dim3(256), 0, st, c, p, ws, out);
+  else
+    hipLaunchKernelGGL(combine_kernel<kChunk>, dim3(c.B * p.Hq), dim3(256), 0, st, c, p, ws, out);
   return hipGetLastError();
 }
 

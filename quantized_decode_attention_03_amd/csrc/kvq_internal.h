@@ -64,6 +64,7 @@ struct AttnPlan {
   int64_t units;               // 32-token tiles of all (sequence, KV head) pairs
   int n_wg;                    // attention workgroups (each takes units / n_wg)
   int need_combine;            // some pair spans several workgroups, or a sequence is empty
+  int max_pieces;              // the most workgroups any one pair spans
   int rope;                    // keys cached before the rotary embedding
   double rope_log2_theta;      // log2 of its frequency base
 };
