@@ -40,16 +40,20 @@ struct GroupQ {
 };
 
 // rint(x / s) with x / s the correctly rounded fp32 quotient, given r =
-// 1/s to within 1 ulp. y = x * r is within 2^-22 |x/s| of that quotient, so
-// for |y| < 2^12 it is within 2^-10 of it: when y is more than 2^-9 from the
-// nearest half-integer both round to the same integer; otherwise (or for a
-// large quotient) the true division decides.
+// 1/s to within 1 ulp, for |x / s| < 2^12 (every caller: a group's codes lie
+// within 2^11 + 2^8 steps of zero). y = x * r is within 2^-22 |x/s| < 2^-10 of
+// that quotient, so when y is more than 2^-9 from the nearest half-integer both
+// round to the same integer; otherwise the true division decides. That case
+// is rare (about one element in 256), so the division sits behind a
+// wave-uniform branch: the wavefront skips it unless one of its lanes needs it.
 __device__ __forceinline__ float div_rint(float x, float s, float r) {
 #pragma clang fp contract(off)
   const float y = x * r;
-  const float k = __builtin_rintf(y);
-  const float d = __builtin_fabsf(y - k);
-  if (__builtin_fabsf(y) >= 4096.0f || __builtin_fabsf(d - 0.5f) < 0.001953125f) return __builtin_rintf(x / s);
+  float k = __builtin_rintf(y);
+  const bool near_half = __builtin_fabsf(y - k) > 0.498046875f;  // 1/2 - 2^-9
+  if (__builtin_amdgcn_ballot_w64(near_half)) {
+    if (near_half) k = __builtin_rintf(x / s);
+  }
   return k;
 }
 
@@ -84,12 +88,12 @@ __device__ __forceinline__ GroupQ group_params(float xmin, float xmax, int bits)
   return g;
 }
 
-// Stored unsigned code u = q - q_min of one element.
+// Stored unsigned code u = q - q_min of one element: rint(x / s) + (z - q_min)
+// clamped to [0, q_max - q_min] (integers, exact in fp32).
 __device__ __forceinline__ uint32_t quant_code(float x, const GroupQ& g, int bits) {
 #pragma clang fp contract(off)
-  float q = div_rint(x, g.s, g.r) + g.z;
-  q = __builtin_fminf(__builtin_fmaxf(q, (float)qmin_of(bits)), (float)qmax_of(bits));
-  return (uint32_t)((int)q - qmin_of(bits));
+  const float u = div_rint(x, g.s, g.r) + (g.z - (float)qmin_of(bits));
+  return (uint32_t)__builtin_amdgcn_fmed3f(u, 0.0f, (float)(qmax_of(bits) - qmin_of(bits)));
 }
 
 // Exact fp32 reconstruction s * (q - z) from a stored code and a meta word.
